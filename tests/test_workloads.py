@@ -1,0 +1,84 @@
+"""The seeded generator: determinism and the mask / pad / outlier structure of
+each workload.  CPU only."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from gqa_decode_attention_fr_amd import workloads as W
+
+NEG_INF = 0xFC00
+
+
+def test_same_seed_same_bytes():
+    a = W.generate(W.CAUSAL_TAIL)
+    b = W.generate(W.CAUSAL_TAIL)
+    for key in ("q", "k", "v", "mask", "outlier_rows"):
+        assert np.array_equal(a[key], b[key])
+    c = W.generate(W.CAUSAL_TAIL, seed=1)
+    assert not np.array_equal(a["q"], c["q"])
+
+
+@pytest.mark.parametrize("w", W.WORKLOADS[:4], ids=lambda w: w.name)
+def test_shapes_and_dtypes(w):
+    g = W.generate(w)
+    qdt = np.uint16 if w.q_dtype == "f16" else np.float32
+    assert g["q"].dtype == qdt and g["q"].shape == (w.n_inst, w.n_tok, w.n_head, w.hd)
+    assert g["k"].shape == g["v"].shape == (w.n_inst, w.n_kv, w.hd)
+    assert g["k"].dtype == g["v"].dtype == np.uint16
+    assert g["mask"].shape == (w.n_inst, w.n_tok, w.n_kv)
+    # pad rows are zero, valid rows are not
+    assert not g["k"][:, w.n_valid:].any() and not g["v"][:, w.n_valid:].any()
+    assert (np.abs(g["k"][:, :w.n_valid].view(np.float16).astype(np.float32)).sum(-1) > 0).all()
+
+
+def test_pad_mask_structure():
+    w = W.PI05_ACTION_STEP
+    m = W.build_mask(w)
+    assert (m[:, :w.n_valid] == 0).all() and (m[:, w.n_valid:] == NEG_INF).all()
+    assert w.n_inst == 18 and w.n_valid == 968 and w.n_kv == 1024
+
+
+def test_causal_tail_mask():
+    w = W.CAUSAL_TAIL
+    m = W.build_mask(w)
+    base = w.n_kv - w.n_tok
+    assert (m[:, :base] == 0).all()
+    for t in range(w.n_tok):
+        for i in range(w.n_tok):
+            assert m[t, base + i] == (0 if i <= t else NEG_INF)
+
+
+def test_causal_tail_outlier_rows_scaled_by_eight():
+    w = W.CAUSAL_TAIL
+    g = W.generate(w)
+    plain = W.generate(dataclasses.replace(w, k_outlier_scale=1.0))
+    rows = g["outlier_rows"][0]
+    assert rows.size == round(0.05 * 2048) == 102 and np.unique(rows).size == 102
+    kf = g["k"][0].view(np.float16).astype(np.float64)
+    pf = plain["k"][0].view(np.float16).astype(np.float64)
+    assert np.array_equal(kf[rows], 8.0 * pf[rows])
+    others = np.setdiff1d(np.arange(w.n_kv), rows)
+    assert np.array_equal(kf[others], pf[others])
+
+
+def test_q16_workload_is_rounded_from_f32():
+    w = W.H16_HD128_Q16
+    g = W.generate(w)
+    f32 = W.generate(dataclasses.replace(w, q_dtype="f32"))
+    assert np.array_equal(g["q"], f32["q"].astype(np.float16).view(np.uint16))
+
+
+def test_value_distributions():
+    g = W.generate(W.PI05_ACTION_STEP)
+    kv = g["k"][:, :968].view(np.float16).astype(np.float64)
+    assert abs(kv.std() - 0.5) < 0.01  # N(0, 0.5) read as std 0.5
+    q = g["q"].astype(np.float64)
+    assert abs(q.std() - 1.0) < 0.01
+
+
+def test_byte_and_flop_accounting():
+    w = W.LONG_CONTEXT
+    kv = 2 * 32000 * 128 * 2
+    assert w.algorithmic_bytes() == kv + 512 * 128 * 4 + 16 * 32768 * 2 + 512 * 128 * 4
+    assert w.flops() == 4 * 512 * 32000 * 128
