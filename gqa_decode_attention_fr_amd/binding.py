@@ -1,0 +1,165 @@
+"""Thin ctypes binding over libfrattn.so (include/fr_decode_attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  Functions carry the C entry points' names, take
+torch CUDA tensors (or raw device addresses as ints) and the current torch
+stream by default, and raise FrError on a non-zero status.  There is no
+fallback: if the library is missing this module raises when first used.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfrattn.so")
+
+FR_OK = 0
+FR_ERR_INVALID = -1
+FR_ERR_UNSUPPORTED = -2
+FR_ERR_CAPTURE = -3
+FR_ERR_HIP = -4
+FR_ERR_WORKSPACE = -5
+
+FR_Q_F32 = 0
+FR_Q_F16 = 1
+
+FR_Q_ROUND_F16 = 0x1
+FR_VARIANT_FUSED = 0x2
+FR_VARIANT_DECOMPOSED = 0x4
+
+# Every symbol the header declares (checked by the ABI tests).
+EXPORTED = ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
+            "fr_decode_attn_ex", "fr_decode_attn_workspace_size", "fr_decode_attn_reserve",
+            "fr_decode_attn_plan", "fr_status_str", "fr_abi_version")
+
+PLAN_FIELDS = ("variant", "n_split", "chunk", "waves", "tiles", "n_rowblk", "grid", "launches")
+
+
+class FrError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m gqa_decode_attention_fr_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, u32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                  ctypes.c_float, ctypes.c_uint, ctypes.c_size_t)
+    single = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+    lib.fr_decode_attn.argtypes = single
+    lib.fr_decode_attn_q16.argtypes = single
+    batched = [vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, i32, i32, i32, f32]
+    lib.fr_decode_attn_batched.argtypes = batched + [vp]
+    lib.fr_decode_attn_ex.argtypes = batched + [u32, vp, sz, vp]
+    for fn in ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
+               "fr_decode_attn_ex", "fr_decode_attn_reserve", "fr_decode_attn_plan",
+               "fr_abi_version"):
+        getattr(lib, fn).restype = i32
+    lib.fr_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32,
+                                                  ctypes.POINTER(i32)]
+    lib.fr_decode_attn_workspace_size.restype = sz
+    lib.fr_decode_attn_reserve.argtypes = [i32, i32, i32, i32, i32, u32]
+    lib.fr_decode_attn_plan.argtypes = [i32, i32, i32, i32, i32, u32, ctypes.POINTER(i32), i32]
+    lib.fr_status_str.argtypes = [i32]
+    lib.fr_status_str.restype = ctypes.c_char_p
+    lib.fr_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().fr_status_str(int(status)).decode()
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(st: int, what: str) -> None:
+    if st != FR_OK:
+        raise FrError(st, what)
+
+
+def fr_decode_attn(q, k, v, mask, out, n_head, n_tok, n_kv, hd, scale, stream=None) -> None:
+    """f32 q [n_tok, n_head, hd]; f16 k, v [n_kv, hd]; f16 mask [n_tok, n_kv] or None;
+    fp32 out [n_tok, n_head, hd]."""
+    _check(load().fr_decode_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out), n_head,
+                                 n_tok, n_kv, hd, scale, _stream(stream)), "fr_decode_attn")
+
+
+def fr_decode_attn_q16(q16, k, v, mask, out, n_head, n_tok, n_kv, hd, scale,
+                       stream=None) -> None:
+    """Pre-rounded f16 q [n_tok, n_head, hd]; otherwise as fr_decode_attn."""
+    _check(load().fr_decode_attn_q16(_ptr(q16), _ptr(k), _ptr(v), _ptr(mask), _ptr(out),
+                                     n_head, n_tok, n_kv, hd, scale, _stream(stream)),
+           "fr_decode_attn_q16")
+
+
+def fr_decode_attn_batched(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride,
+                           mask_stride, out_stride, n_head, n_tok, n_kv, hd, scale,
+                           stream=None) -> None:
+    _check(load().fr_decode_attn_batched(_ptr(q), q_format, _ptr(k), _ptr(v), _ptr(mask),
+                                         _ptr(out), n_inst, q_stride, kv_stride, mask_stride,
+                                         out_stride, n_head, n_tok, n_kv, hd, scale,
+                                         _stream(stream)), "fr_decode_attn_batched")
+
+
+def fr_decode_attn_ex(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride,
+                      out_stride, n_head, n_tok, n_kv, hd, scale, flags=0, workspace=None,
+                      workspace_bytes=0, stream=None) -> None:
+    _check(load().fr_decode_attn_ex(_ptr(q), q_format, _ptr(k), _ptr(v), _ptr(mask), _ptr(out),
+                                    n_inst, q_stride, kv_stride, mask_stride, out_stride, n_head,
+                                    n_tok, n_kv, hd, scale, flags, _ptr(workspace),
+                                    workspace_bytes, _stream(stream)), "fr_decode_attn_ex")
+
+
+def fr_decode_attn_workspace_size(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> int:
+    st = ctypes.c_int(0)
+    n = load().fr_decode_attn_workspace_size(n_inst, n_head, n_tok, n_kv, hd, flags,
+                                             ctypes.byref(st))
+    _check(st.value, "fr_decode_attn_workspace_size")
+    return int(n)
+
+
+def fr_decode_attn_reserve(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> None:
+    _check(load().fr_decode_attn_reserve(n_inst, n_head, n_tok, n_kv, hd, flags),
+           "fr_decode_attn_reserve")
+
+
+def fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> dict:
+    info = (ctypes.c_int * len(PLAN_FIELDS))()
+    _check(load().fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags, info,
+                                      len(PLAN_FIELDS)), "fr_decode_attn_plan")
+    return dict(zip(PLAN_FIELDS, list(info)))
+
+
+def fr_status_str(status: int) -> str:
+    return status_str(status)
+
+
+def fr_abi_version() -> int:
+    return int(load().fr_abi_version())

@@ -1,0 +1,333 @@
+// fr_api.hip -- the exported C ABI (include/fr_decode_attn.h): argument checks,
+// launch planning, the grow-only device workspace, and dispatch.
+//
+// Argument checks play the role of the window predicate in the FlashRT-llama.cpp
+// development guide (section "Adding a fusion window"): every assumption the
+// kernels make -- dtypes, shapes, element strides, alignment, the absence of
+// aliasing -- is pinned here, and anything else is declined with a status code
+// before any HIP call is made.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
+
+#include "fr_decode_attn.h"
+#include "fr_internal.h"
+
+namespace fr {
+
+int tiles_per_wave(int hd);
+
+int env_int(const char *name, int fallback) {
+  const char *s = std::getenv(name);
+  if (!s || !*s) return fallback;
+  return std::atoi(s);
+}
+
+bool debug_on() { return env_int("FR_DEBUG", 0) != 0; }
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroups the split kernel should launch to cover the machine: 256 compute
+// units on MI355X, one resident workgroup per unit at these LDS sizes.
+constexpr int kTargetWorkgroups = 256;
+
+int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flags, Plan *plan) {
+  Plan p;
+  const int M = n_head * n_tok;
+  p.variant = (flags & FR_VARIANT_DECOMPOSED) ? kDecomposed : kFused;
+  const int tiles = tiles_per_wave(hd);
+  const int tiles_total = (int)cdiv(M, 16);
+  const int waves_needed = (int)cdiv(tiles_total, tiles);
+  p.tiles = tiles;
+  // fused: 4..8 waves share each LDS block; decomposed kernels use 4 waves
+  p.waves = p.variant == kDecomposed ? 4 : std::min(8, std::max(4, waves_needed));
+  const int rows_per_wg = p.waves * tiles * 16;
+  p.n_rowblk = (int)cdiv(M, rows_per_wg);
+  const int key_blocks = (int)cdiv(n_kv, kKeyBlock);
+  int want = (int)std::max<int64_t>(1, cdiv(kTargetWorkgroups, (int64_t)n_inst * p.n_rowblk));
+  const int forced = env_int("FR_FORCE_SPLITS", 0);
+  if (forced > 0) want = forced;
+  want = std::min(std::max(want, 1), key_blocks);
+  const int blocks_per_split = (int)cdiv(key_blocks, want);
+  p.chunk = blocks_per_split * kKeyBlock;
+  p.n_split = (int)cdiv(key_blocks, blocks_per_split);
+  p.grid = n_inst * p.n_rowblk * p.n_split;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)n_inst * p.n_split * M;
+  if (p.variant == kFused) {
+    p.launches = p.n_split > 1 ? 2 : 1;
+    p.ws_bytes = p.n_split > 1 ? al(rows * hd * sizeof(float) + rows * 2 * sizeof(float)) : 0;
+  } else {
+    // [PV partials when split] [scores fp32 M x kv_pad] [probabilities f16 M x kv_pad]
+    const size_t kv_pad = (size_t)key_blocks * kKeyBlock;
+    p.launches = 3 + (p.n_split > 1 ? 1 : 0);
+    p.ws_bytes = (p.n_split > 1 ? al(rows * hd * sizeof(float)) : 0) +
+                 al((size_t)n_inst * M * kv_pad * sizeof(float)) +
+                 al((size_t)n_inst * M * kv_pad * sizeof(uint16_t));
+  }
+  *plan = p;
+  return FR_OK;
+}
+
+}  // namespace fr
+
+using fr::Plan;
+using fr::Problem;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi; // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range span(const void *base, int n_inst, int64_t stride, int64_t elems, size_t esize) {
+  const uintptr_t lo = (uintptr_t)base;
+  const int64_t last = (int64_t)(n_inst - 1) * stride + elems;
+  return Range{lo, lo + (uintptr_t)(last * (int64_t)esize)};
+}
+
+int check_sizes(int n_inst, int n_head, int n_tok, int n_kv, int hd) {
+  if (n_inst < 1 || n_head < 1 || n_tok < 1 || n_kv < 1 || hd < 1) return FR_ERR_INVALID;
+  if (n_tok > FR_MAX_TOKENS || n_head > FR_MAX_HEADS) return FR_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
+  if (n_kv > (1 << 26)) return FR_ERR_UNSUPPORTED;
+  if ((int64_t)n_inst * n_head * n_tok > (1 << 24)) return FR_ERR_UNSUPPORTED;
+  return FR_OK;
+}
+
+int check_flags(int q_format, unsigned flags) {
+  const unsigned known = FR_Q_ROUND_F16 | FR_VARIANT_FUSED | FR_VARIANT_DECOMPOSED;
+  if (flags & ~known) return FR_ERR_INVALID;
+  if ((flags & FR_VARIANT_FUSED) && (flags & FR_VARIANT_DECOMPOSED)) return FR_ERR_INVALID;
+  if (q_format != FR_Q_F32 && q_format != FR_Q_F16) return FR_ERR_INVALID;
+  if (q_format == FR_Q_F16 && (flags & FR_Q_ROUND_F16)) return FR_ERR_INVALID;
+  return FR_OK;
+}
+
+int validate(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
+             const uint16_t *mask, const float *out, int n_inst, int64_t q_stride,
+             int64_t kv_stride, int64_t mask_stride, int64_t out_stride, int n_head, int n_tok,
+             int n_kv, int hd, float scale, unsigned flags) {
+  if (!q || !k || !v || !out) return FR_ERR_INVALID;
+  int st = check_sizes(n_inst, n_head, n_tok, n_kv, hd);
+  if (st != FR_OK) return st;
+  st = check_flags(q_format, flags);
+  if (st != FR_OK) return st;
+  if (!std::isfinite(scale)) return FR_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return FR_ERR_INVALID;
+  if (mask && !aligned(mask, 2)) return FR_ERR_INVALID;
+  const int64_t M = (int64_t)n_head * n_tok;
+  const size_t qsize = q_format == FR_Q_F16 ? 2 : 4;
+  if (n_inst > 1) {
+    if (q_stride < 0 || (q_stride != 0 && q_stride < M * hd)) return FR_ERR_INVALID;
+    if ((q_stride * (int64_t)qsize) % 16) return FR_ERR_INVALID;
+    if (kv_stride < 0 || (kv_stride != 0 && kv_stride < (int64_t)n_kv * hd)) return FR_ERR_INVALID;
+    if ((kv_stride * 2) % 16) return FR_ERR_INVALID;
+    if (mask_stride < 0 || (mask_stride != 0 && mask_stride < (int64_t)n_tok * n_kv))
+      return FR_ERR_INVALID;
+    if (out_stride < M * hd || (out_stride * 4) % 16) return FR_ERR_INVALID;
+  } else {
+    q_stride = kv_stride = mask_stride = out_stride = 0;
+  }
+  const Range ro = span(out, n_inst, out_stride, M * hd, 4);
+  if (overlaps(ro, span(q, n_inst, q_stride, M * hd, qsize))) return FR_ERR_INVALID;
+  if (overlaps(ro, span(k, n_inst, kv_stride, (int64_t)n_kv * hd, 2))) return FR_ERR_INVALID;
+  if (overlaps(ro, span(v, n_inst, kv_stride, (int64_t)n_kv * hd, 2))) return FR_ERR_INVALID;
+  if (mask && overlaps(ro, span(mask, n_inst, mask_stride, (int64_t)n_tok * n_kv, 2)))
+    return FR_ERR_INVALID;
+  return FR_OK;
+}
+
+// ---- library-owned, per-device, grow-only workspace
+struct DeviceWs {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::vector<DeviceWs> g_ws;
+
+size_t round_ws(size_t need) {
+  const size_t mb = (size_t)1 << 20;
+  return (need + mb - 1) / mb * mb;
+}
+
+// Returns a workspace of at least `need` bytes on the current device.  Grows
+// only outside graph capture (FR_ERR_CAPTURE otherwise).
+int library_ws(size_t need, hipStream_t stream, bool check_capture, void **out) {
+  *out = nullptr;
+  if (need == 0) return FR_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  DeviceWs &w = g_ws[dev];
+  if (w.bytes >= need) {
+    *out = w.ptr;
+    return FR_OK;
+  }
+  if (check_capture) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return FR_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return FR_ERR_CAPTURE;
+  }
+  if (w.ptr) {
+    // earlier calls may still be reading the old buffer
+    if (hipDeviceSynchronize() != hipSuccess) return FR_ERR_HIP;
+    if (hipFree(w.ptr) != hipSuccess) return FR_ERR_HIP;
+    w.ptr = nullptr;
+    w.bytes = 0;
+  }
+  const size_t bytes = round_ws(need);
+  void *p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) return FR_ERR_HIP;
+  w.ptr = p;
+  w.bytes = bytes;
+  *out = p;
+  return FR_OK;
+}
+
+int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const uint16_t *mask,
+        float *out, int n_inst, int64_t q_stride, int64_t kv_stride, int64_t mask_stride,
+        int64_t out_stride, int n_head, int n_tok, int n_kv, int hd, float scale,
+        unsigned flags, void *workspace, size_t workspace_bytes, bool caller_ws,
+        void *stream) {
+  int st = validate(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride,
+                    out_stride, n_head, n_tok, n_kv, hd, scale, flags);
+  if (st != FR_OK) return st;
+  if (n_inst == 1) q_stride = kv_stride = mask_stride = out_stride = 0;
+  Plan plan;
+  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &plan);
+  if (st != FR_OK) return st;
+  if (caller_ws) {
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+      return FR_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 256)) return FR_ERR_INVALID;
+  } else {
+    st = library_ws(plan.ws_bytes, (hipStream_t)stream, true, &workspace);
+    if (st != FR_OK) return st;
+  }
+  Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.mask = mask;
+  p.out = out;
+  p.n_inst = n_inst;
+  p.q_stride = q_stride;
+  p.kv_stride = kv_stride;
+  p.mask_stride = mask_stride;
+  p.out_stride = out_stride == 0 ? (int64_t)n_head * n_tok * hd : out_stride;
+  p.n_head = n_head;
+  p.n_tok = n_tok;
+  p.n_kv = n_kv;
+  p.hd = hd;
+  p.scale = scale;
+  p.qmode = q_format == FR_Q_F16 ? fr::kQF16 : ((flags & FR_Q_ROUND_F16) ? fr::kQRound : fr::kQHiLo);
+  if (fr::debug_on())
+    std::fprintf(stderr,
+                 "[fr_decode_attn] variant=%d n_inst=%d M=%d n_kv=%d hd=%d qmode=%d splits=%d "
+                 "chunk=%d waves=%d tiles=%d rowblk=%d grid=%d ws=%zu\n",
+                 plan.variant, n_inst, n_head * n_tok, n_kv, hd, p.qmode, plan.n_split,
+                 plan.chunk, plan.waves, plan.tiles, plan.n_rowblk, plan.grid, plan.ws_bytes);
+  hipError_t err = plan.variant == fr::kDecomposed
+                       ? fr::launch_decomposed(p, plan, workspace, (hipStream_t)stream)
+                       : fr::launch_fused(p, plan, workspace, (hipStream_t)stream);
+  return err == hipSuccess ? FR_OK : FR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fr_decode_attn(const float *q, const uint16_t *k, const uint16_t *v, const uint16_t *mask,
+                   float *out, int n_head, int n_tok, int n_kv, int hd, float scale,
+                   void *stream) {
+  return run(q, FR_Q_F32, k, v, mask, out, 1, 0, 0, 0, 0, n_head, n_tok, n_kv, hd, scale, 0u,
+             nullptr, 0, false, stream);
+}
+
+int fr_decode_attn_q16(const uint16_t *q16, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *mask, float *out, int n_head, int n_tok, int n_kv, int hd,
+                       float scale, void *stream) {
+  return run(q16, FR_Q_F16, k, v, mask, out, 1, 0, 0, 0, 0, n_head, n_tok, n_kv, hd, scale, 0u,
+             nullptr, 0, false, stream);
+}
+
+int fr_decode_attn_batched(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
+                           const uint16_t *mask, float *out, int n_inst, int64_t q_stride,
+                           int64_t kv_stride, int64_t mask_stride, int64_t out_stride,
+                           int n_head, int n_tok, int n_kv, int hd, float scale, void *stream) {
+  return run(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride, out_stride,
+             n_head, n_tok, n_kv, hd, scale, 0u, nullptr, 0, false, stream);
+}
+
+int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
+                      const uint16_t *mask, float *out, int n_inst, int64_t q_stride,
+                      int64_t kv_stride, int64_t mask_stride, int64_t out_stride, int n_head,
+                      int n_tok, int n_kv, int hd, float scale, unsigned flags, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return run(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride, out_stride,
+             n_head, n_tok, n_kv, hd, scale, flags, workspace, workspace_bytes,
+             workspace != nullptr, stream);
+}
+
+size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv, int hd,
+                                     unsigned flags, int *status) {
+  int st = check_sizes(n_inst, n_head, n_tok, n_kv, hd);
+  if (st == FR_OK) st = check_flags(FR_Q_F32, flags & ~FR_Q_ROUND_F16);
+  Plan plan;
+  if (st == FR_OK) st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &plan);
+  if (status) *status = st;
+  return st == FR_OK ? plan.ws_bytes : 0;
+}
+
+int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
+                           unsigned flags) {
+  int st = FR_OK;
+  const size_t need = fr_decode_attn_workspace_size(n_inst, n_head, n_tok, n_kv, hd, flags, &st);
+  if (st != FR_OK) return st;
+  void *p = nullptr;
+  return library_ws(need, nullptr, false, &p);
+}
+
+int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flags,
+                        int *info, int n_info) {
+  if (!info || n_info < 0) return FR_ERR_INVALID;
+  int st = check_sizes(n_inst, n_head, n_tok, n_kv, hd);
+  if (st == FR_OK) st = check_flags(FR_Q_F32, flags & ~FR_Q_ROUND_F16);
+  if (st != FR_OK) return st;
+  Plan p;
+  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &p);
+  if (st != FR_OK) return st;
+  const int vals[8] = {p.variant, p.n_split, p.chunk, p.waves,
+                       p.tiles,   p.n_rowblk, p.grid, p.launches};
+  for (int i = 0; i < n_info && i < 8; ++i) info[i] = vals[i];
+  return FR_OK;
+}
+
+const char *fr_status_str(int status) {
+  switch (status) {
+    case FR_OK: return "FR_OK";
+    case FR_ERR_INVALID: return "FR_ERR_INVALID: bad pointer, size, stride, alignment or aliasing";
+    case FR_ERR_UNSUPPORTED: return "FR_ERR_UNSUPPORTED: shape outside the supported window";
+    case FR_ERR_CAPTURE: return "FR_ERR_CAPTURE: workspace must grow while the stream is captured";
+    case FR_ERR_HIP: return "FR_ERR_HIP: HIP runtime or launch failure";
+    case FR_ERR_WORKSPACE: return "FR_ERR_WORKSPACE: caller workspace too small";
+    default: return "unknown fr_status";
+  }
+}
+
+int fr_abi_version(void) { return FR_DECODE_ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// fr_internal.h -- launch plan and kernel launchers shared by the host API and
+// the kernel translation unit.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fr {
+
+// Keys staged through LDS per block iteration of the split kernel.
+constexpr int kKeyBlock = 64;
+// Largest query-token count (the pages' window covers q_tokens <= 16).
+constexpr int kMaxTok = 16;
+
+enum Variant { kFused = 1, kDecomposed = 2 };
+enum QMode { kQHiLo = 0, kQF16 = 1, kQRound = 2 };
+
+struct Plan {
+  int variant = kFused;
+  int n_split = 1;     // key splits per instance
+  int chunk = 0;       // keys per split (multiple of kKeyBlock)
+  int waves = 4;       // waves per workgroup of the split kernel
+  int tiles = 1;       // 16-row tiles per wave
+  int n_rowblk = 1;    // row blocks per instance
+  int grid = 0;        // workgroups of the split kernel
+  int launches = 1;    // kernel launches per call
+  size_t ws_bytes = 0; // device workspace bytes
+};
+
+// Everything one launch sequence needs.  Strides count elements.
+struct Problem {
+  const void *q;
+  const uint16_t *k;
+  const uint16_t *v;
+  const uint16_t *mask;
+  float *out;
+  int n_inst;
+  int64_t q_stride, kv_stride, mask_stride, out_stride;
+  int n_head, n_tok, n_kv, hd;
+  float scale;
+  int qmode;
+};
+
+// Chooses the variant and the work decomposition (pure host logic).
+int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flags, Plan *plan);
+
+// Enqueue the fused split-KV path (split kernel, plus the combine kernel when
+// n_split > 1).  Returns hipSuccess or the launch error.
+hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hipStream_t stream);
+
+// Enqueue the three-launch decomposition: QK^T, masked softmax, PV.
+hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace,
+                             hipStream_t stream);
+
+}  // namespace fr

@@ -1,0 +1,181 @@
+/*
+ * fr_decode_attn.h -- C ABI of the MI355X (gfx950) small-q GQA decode attention.
+ *
+ * The operation.  FlashRT pull request #185, "feat(structures): ggml host
+ * adapter -- llama.cpp distribution for pi0.5 on Thor (SM110)", in the commit
+ * that introduces the decomposed decode attention: FLASH_ATTN_EXT with at
+ * most 16 query tokens over a single padded f16 KV head is computed as a
+ * QK^T contraction, a masked softmax accurate to fp32, and a PV contraction
+ * whose fp32 result lands in the node's [hd, n_head, n_tok] destination.
+ * For every query token t < n_tok, head h < n_head and d < hd:
+ *
+ *     s_j           = scale * sum_e q[t][h][e] * K[j][e] + mask[t][j]   (j < n_kv)
+ *     out[t][h][d]  = sum_j exp(s_j - max s) * V[j][d] / sum_j exp(s_j - max s)
+ *
+ * Layouts (element offsets, fastest index last, all dense):
+ *   q    [n_tok][n_head][hd]  -- "t-major" rows r = t*n_head + h.  The same
+ *                                pull request's GQA-collapse commit orders the
+ *                                n_head*n_tok query rows this way so that one
+ *                                contraction covers every head; its qkv_post
+ *                                handoff commit stores Q in exactly this order.
+ *   k, v [n_kv][hd]           -- IEEE binary16 bits, the one KV head that all
+ *                                query heads share (GQA with one KV group).
+ *                                Pad rows (keys the mask hides for every token)
+ *                                may hold any finite values; zero is usual.
+ *   mask [n_tok][n_kv]        -- IEEE binary16 bits, additive, one row per query
+ *                                token, shared by every head: 0 keeps a key,
+ *                                -inf hides it; other finite values are added
+ *                                to the logit.  NULL means all zero.
+ *   out  [n_tok][n_head][hd]  -- fp32; this is ggml's [hd, n_head, n_tok]
+ *                                (fastest first), written contiguously.
+ *
+ * Readings the pages leave open, fixed by this library:
+ *   - scale multiplies q.K before the mask is added;
+ *   - a row whose keys are all hidden gets an all-zero output row;
+ *   - f32 queries are used at fp32 accuracy: each q is split into two f16
+ *     parts (hi = f16(q), lo = f16(q - hi)) that both enter the f16 matrix
+ *     cores, so q.K carries ~22 significand bits.  FR_Q_ROUND_F16 instead
+ *     rounds q to f16 once, the way the pages' gather kernel does.
+ *   - |q| must stay below 65504 (the f16 range); inputs holding NaN or inf
+ *     give unspecified output.
+ *
+ * Pointers.  Every tensor pointer is a DEVICE pointer owned by the caller; the
+ * library never frees or retains it past the call.  q, k, v and out must be
+ * 16-byte aligned; mask needs 2-byte alignment.  Inputs are never written.
+ * out must not overlap any input.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ * Every entry point only enqueues work on that stream: it does not
+ * synchronise and returns before the result exists.  Entry points never abort
+ * the process; failures come back as an fr_status code.  Argument checks run
+ * before any HIP call, so a rejected call launches nothing.
+ *
+ * Workspace.  Shapes that split the key range across workgroups keep partial
+ * results in a device workspace.  With workspace == NULL (all entry points but
+ * fr_decode_attn_ex) the library uses its own per-device buffer, which only
+ * grows and is never allocated while `stream` is being captured into a graph
+ * (the capture-safety rule of the FlashRT-llama.cpp development guide,
+ * section "Caches (all capture-safe)"): a call that would need to grow it
+ * during capture returns FR_ERR_CAPTURE; call fr_decode_attn_reserve before
+ * capturing.  Calls that share the library workspace must be ordered on one
+ * stream (or otherwise serialised); concurrent calls on different streams of
+ * one device must each pass their own workspace to fr_decode_attn_ex.
+ */
+#ifndef FR_DECODE_ATTN_H
+#define FR_DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+typedef enum fr_status {
+    FR_OK = 0,
+    FR_ERR_INVALID = -1,     /* null/misaligned pointer, bad size or stride, out overlaps an input */
+    FR_ERR_UNSUPPORTED = -2, /* n_tok outside 1..16, hd not 64/128/256, n_head outside 1..1024 */
+    FR_ERR_CAPTURE = -3,     /* the library workspace would have to grow while the stream is captured */
+    FR_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+    FR_ERR_WORKSPACE = -5    /* the caller's workspace is smaller than fr_decode_attn_workspace_size */
+} fr_status;
+
+/* Query formats for fr_decode_attn_batched / fr_decode_attn_ex. */
+#define FR_Q_F32 0 /* q is float32 */
+#define FR_Q_F16 1 /* q is binary16 bits, already rounded (the qkv_post f16 handoff) */
+
+/* Flags for fr_decode_attn_ex. */
+#define FR_Q_ROUND_F16 0x1u        /* f32 q: round to f16 once, as the pages' gather does */
+#define FR_VARIANT_FUSED 0x2u      /* force the fused single-pass split-KV variant */
+#define FR_VARIANT_DECOMPOSED 0x4u /* force the three-launch QK^T -> softmax -> PV variant */
+
+/* Limits checked by every entry point. */
+#define FR_MAX_TOKENS 16    /* the pages' window covers q_tokens <= 16 */
+#define FR_MAX_HEADS 1024
+
+/*
+ * f32 queries.  q: float32 [n_tok][n_head][hd]; k, v, mask, out as above.
+ * The decomposed decode attention commit of FlashRT PR #185 defines the
+ * operation; q is used at fp32 accuracy (hi/lo f16 split).
+ * Returns FR_OK or a negative fr_status.
+ */
+int fr_decode_attn(const float *q, const uint16_t *k, const uint16_t *v,
+                   const uint16_t *mask, float *out, int n_head, int n_tok,
+                   int n_kv, int hd, float scale, void *stream);
+
+/*
+ * Pre-rounded f16 queries: the qkv_post handoff commit of FlashRT PR #185,
+ * where the producer stores the rope'd and scaled Q rows as f16 in the t-major
+ * order this window reads, so no gather step runs.  q16: binary16 bits
+ * [n_tok][n_head][hd].  fr_decode_attn_q16(f16_rne(q)) equals
+ * fr_decode_attn_ex(q, FR_Q_F32, ..., FR_Q_ROUND_F16, ...) bit for bit.
+ */
+int fr_decode_attn_q16(const uint16_t *q16, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *mask, float *out, int n_head, int n_tok,
+                       int n_kv, int hd, float scale, void *stream);
+
+/*
+ * n_inst independent instances (e.g. the layers of one model step) in one
+ * launch sequence.  Instance i reads q + i*q_stride, k + i*kv_stride,
+ * v + i*kv_stride, mask + i*mask_stride and writes out + i*out_stride; strides
+ * count ELEMENTS of each tensor's type.  q_stride and kv_stride may be 0
+ * (shared input); mask_stride may be 0 (one mask for all); out_stride must be
+ * at least n_tok*n_head*hd.  Non-zero strides must keep 16-byte alignment
+ * (mask: any).  q_format is FR_Q_F32 or FR_Q_F16.
+ */
+int fr_decode_attn_batched(const void *q, int q_format, const uint16_t *k,
+                           const uint16_t *v, const uint16_t *mask, float *out,
+                           int n_inst, int64_t q_stride, int64_t kv_stride,
+                           int64_t mask_stride, int64_t out_stride, int n_head,
+                           int n_tok, int n_kv, int hd, float scale, void *stream);
+
+/*
+ * Everything: batched instances, flags (FR_Q_ROUND_F16, FR_VARIANT_*), and an
+ * optional caller-owned device workspace.  workspace == NULL uses the library
+ * workspace (grow-only, see above); otherwise it must be 256-byte aligned and
+ * at least fr_decode_attn_workspace_size(...) bytes, else FR_ERR_WORKSPACE.
+ * The library keeps no reference to a caller workspace after the call's
+ * kernels finish.
+ */
+int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k,
+                      const uint16_t *v, const uint16_t *mask, float *out,
+                      int n_inst, int64_t q_stride, int64_t kv_stride,
+                      int64_t mask_stride, int64_t out_stride, int n_head,
+                      int n_tok, int n_kv, int hd, float scale, unsigned flags,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device workspace bytes a call with these sizes and flags needs (0 if none),
+ * or 0 with *status set when the sizes are rejected (status may be NULL). */
+size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv,
+                                     int hd, unsigned flags, int *status);
+
+/* Grow the library workspace of the CURRENT device so that calls up to these
+ * sizes never allocate.  Synchronous; must not be called during capture.
+ * Returns FR_OK or a negative fr_status. */
+int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
+                           unsigned flags);
+
+/*
+ * The launch plan a call with these sizes would use, for tests and
+ * benchmarks.  Fills up to n_info ints of info[]:
+ *   [0] variant (1 fused, 2 decomposed)  [1] key splits per instance
+ *   [2] keys per split                   [3] waves per workgroup
+ *   [4] 16-row tiles per wave            [5] row blocks per instance
+ *   [6] workgroups of the main kernel    [7] kernel launches per call
+ * Returns FR_OK or a negative fr_status.
+ */
+int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd,
+                        unsigned flags, int *info, int n_info);
+
+/* Static, human-readable name of a status code. */
+const char *fr_status_str(int status);
+
+/* ABI version of this header (bumped on incompatible changes). */
+#define FR_DECODE_ATTN_ABI_VERSION 1
+int fr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FR_DECODE_ATTN_H */

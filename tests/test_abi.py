@@ -1,0 +1,145 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, rejects bad arguments before any HIP call, and plans sensibly."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gqa_decode_attention_fr_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fr_decode_attn.h")
+
+# Fake but 256-byte-aligned device addresses: calls that fail validation never
+# touch them, and these tests only make calls that fail validation.
+Q, K, V, MASK, OUT = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fr_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    declared = header_functions()
+    assert set(declared) == set(B.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for name in declared:
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_header_is_plain_c(tmp_path, lang):
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    src.write_text('#include "fr_decode_attn.h"\nint main(void){return fr_abi_version();}\n')
+    cc = "gcc" if lang == "c" else "g++"
+    subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", f"-I{os.path.dirname(HEADER)}",
+                    str(src)], check=True)
+
+
+def test_abi_version_and_status_strings():
+    assert B.fr_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert B.fr_status_str(st).startswith("FR_")
+    assert "unknown" in B.fr_status_str(7)
+
+
+def call(**kw):
+    a = dict(q=Q, fmt=B.FR_Q_F32, k=K, v=V, mask=MASK, out=OUT, n_inst=1, qs=0, kvs=0, ms=0,
+             os_=0, n_head=8, n_tok=10, n_kv=1024, hd=256, scale=0.0625, flags=0, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    return B.load().fr_decode_attn_ex(a["q"], a["fmt"], a["k"], a["v"], a["mask"], a["out"],
+                                      a["n_inst"], a["qs"], a["kvs"], a["ms"], a["os_"],
+                                      a["n_head"], a["n_tok"], a["n_kv"], a["hd"], a["scale"],
+                                      a["flags"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.FR_ERR_INVALID),
+    (dict(k=None), B.FR_ERR_INVALID),
+    (dict(v=None), B.FR_ERR_INVALID),
+    (dict(out=None), B.FR_ERR_INVALID),
+    (dict(n_tok=0), B.FR_ERR_INVALID),
+    (dict(n_kv=0), B.FR_ERR_INVALID),
+    (dict(n_head=0), B.FR_ERR_INVALID),
+    (dict(n_inst=0), B.FR_ERR_INVALID),
+    (dict(n_tok=17), B.FR_ERR_UNSUPPORTED),
+    (dict(hd=96), B.FR_ERR_UNSUPPORTED),
+    (dict(hd=512), B.FR_ERR_UNSUPPORTED),
+    (dict(n_head=1025), B.FR_ERR_UNSUPPORTED),
+    (dict(q=Q + 8), B.FR_ERR_INVALID),
+    (dict(k=K + 2), B.FR_ERR_INVALID),
+    (dict(out=OUT + 4), B.FR_ERR_INVALID),
+    (dict(mask=MASK + 1), B.FR_ERR_INVALID),
+    (dict(out=Q), B.FR_ERR_INVALID),                       # out aliases q
+    (dict(out=K + 0x1000), B.FR_ERR_INVALID),              # out inside k
+    (dict(scale=float("nan")), B.FR_ERR_INVALID),
+    (dict(scale=float("inf")), B.FR_ERR_INVALID),
+    (dict(flags=0x80), B.FR_ERR_INVALID),
+    (dict(flags=B.FR_VARIANT_FUSED | B.FR_VARIANT_DECOMPOSED), B.FR_ERR_INVALID),
+    (dict(fmt=B.FR_Q_F16, flags=B.FR_Q_ROUND_F16), B.FR_ERR_INVALID),
+    (dict(fmt=2), B.FR_ERR_INVALID),
+    (dict(n_inst=2, os_=100), B.FR_ERR_INVALID),           # out stride < M*hd
+    (dict(n_inst=2, os_=8 * 10 * 256, kvs=5), B.FR_ERR_INVALID),  # kv stride breaks alignment
+    (dict(n_inst=2, os_=8 * 10 * 256, ms=-1), B.FR_ERR_INVALID),
+    (dict(ws=0x900000, ws_bytes=16), B.FR_ERR_WORKSPACE),  # caller workspace too small
+])
+def test_rejected_before_any_launch(kw, status):
+    assert call(**kw) == status
+
+
+def test_single_entry_points_validate_too():
+    lib = B.load()
+    assert lib.fr_decode_attn(None, K, V, MASK, OUT, 8, 1, 64, 256, 0.0625, None) == B.FR_ERR_INVALID
+    assert lib.fr_decode_attn_q16(Q, K, V, MASK, OUT, 8, 17, 64, 256, 0.0625, None) == \
+        B.FR_ERR_UNSUPPORTED
+    assert lib.fr_decode_attn_batched(Q, B.FR_Q_F32, K, V, MASK, OUT, 3, 0, 0, 0, 16, 8, 1, 64,
+                                      256, 0.0625, None) == B.FR_ERR_INVALID
+
+
+SHAPES = [(1, 8, 1, 64, 256), (18, 8, 10, 1024, 256), (1, 16, 16, 4096, 128),
+          (1, 8, 16, 2048, 256), (1, 32, 16, 32768, 128), (3, 5, 7, 1000, 64), (1, 1, 1, 1, 64)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("flags", [0, B.FR_VARIANT_DECOMPOSED])
+def test_plan_covers_keys_and_rows(shape, flags):
+    n_inst, n_head, n_tok, n_kv, hd = shape
+    p = B.fr_decode_attn_plan(*shape, flags)
+    M = n_head * n_tok
+    assert p["variant"] == (2 if flags else 1)
+    assert p["chunk"] % 64 == 0
+    assert p["n_split"] * p["chunk"] >= n_kv > (p["n_split"] - 1) * p["chunk"]  # no empty split
+    assert p["waves"] * p["tiles"] * 16 * p["n_rowblk"] >= M
+    assert p["grid"] == n_inst * p["n_rowblk"] * p["n_split"]
+    assert 4 <= p["waves"] <= 8 and p["tiles"] == {256: 1, 128: 2, 64: 4}[hd]
+    ws = B.fr_decode_attn_workspace_size(*shape, flags)
+    if flags == 0:
+        rows = n_inst * p["n_split"] * M
+        want = 0 if p["n_split"] == 1 else -(-(rows * hd * 4 + rows * 8) // 256) * 256
+        assert ws == want
+        assert p["launches"] == (1 if p["n_split"] == 1 else 2)
+    else:
+        assert ws >= n_inst * M * n_kv * 6 and p["launches"] >= 3
+
+
+def test_forced_split_count(monkeypatch):
+    monkeypatch.setenv("FR_FORCE_SPLITS", "4")
+    p = B.fr_decode_attn_plan(18, 8, 10, 1024, 256, 0)
+    assert p["n_split"] == 4 and p["chunk"] == 256
+
+
+def test_sizes_rejected_by_helpers():
+    with pytest.raises(B.FrError) as e:
+        B.fr_decode_attn_workspace_size(1, 8, 17, 64, 256)
+    assert e.value.status == B.FR_ERR_UNSUPPORTED
+    info = (ctypes.c_int * 8)()
+    assert B.load().fr_decode_attn_plan(1, 8, 1, 64, 96, 0, info, 8) == B.FR_ERR_UNSUPPORTED
