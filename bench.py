@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of small-q GQA decode attention on one MI355X.
+
+One step is one call of the hot path (QK^T, masked softmax, PV, and the
+split combine) over one batch of the workload: for the default pi0.5 action
+step, 18 independent layer instances of n_head=8, n_tok=10, hd=256 and a KV
+head of 1024 keys (968 valid) per call.
+
+Inputs are resident in HBM before timing starts and cold in the caches: every
+call reads a different copy of the batch from a rotating pool of at least
+1 GiB, so neither the 4 MB per-XCD L2 nor the 256 MB MALL can serve it.  The
+K timed calls are queued behind a bounded GPU sleep, so they run back to back
+at device speed rather than at the host's launch rate; HIP events bracket the
+timed region, and the library's event hook brackets each call's main kernel
+on the stream it is launched on.
+
+Prints ONE JSON line (rank 0, one GPU):
+  value      = microseconds per call (lower is better)
+  roofline   = algorithmic bytes of one call / average main-kernel duration,
+               against the 8 TB/s HBM peak
+  cpu_baseline = the fp64 oracle on the host cores, on the same inputs
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and achieved HBM GB/s (% of peak) for small-q GQA decode attention"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense f16 matrix cores
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["gqa_decode_attention_fr_amd/csrc/fr_fused.hip",
+                  "gqa_decode_attention_fr_amd/csrc/fr_device.h",
+                  "gqa_decode_attention_fr_amd/csrc/fr_api.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="pi05_action_step_h8_hd256_t10_kv1024_x18",
+                    help="workload name, or 'all' for one line per workload")
+    ap.add_argument("--variant", choices=["auto", "fused", "decomposed"], default="auto")
+    ap.add_argument("--round-f16", action="store_true", help="f32 Q rounded to f16 once")
+    ap.add_argument("--pool-gib", type=float, default=1.0)
+    ap.add_argument("--warm", action="store_true",
+                    help="also time the same buffers every call (cache-resident, auxiliary)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    return ap.parse_args(argv)
+
+
+class Pool:
+    """R copies of one batch at distinct HBM addresses (one slab per tensor)."""
+
+    def __init__(self, torch, w, g, pool_bytes):
+        n = w.n_inst
+        per = (g["q"].nbytes + g["k"].nbytes + g["v"].nbytes + g["mask"].nbytes
+               + n * w.M * w.hd * 4)
+        self.R = max(2, int(math.ceil(pool_bytes / per)))
+        dev = "cuda"
+
+        def slab(a):
+            t = torch.from_numpy(a.view(np.float16) if a.dtype == np.uint16 else a).to(dev)
+            s = torch.empty((self.R,) + tuple(t.shape), dtype=t.dtype, device=dev)
+            s.copy_(t.unsqueeze(0).expand_as(s))
+            return s
+
+        self.q, self.k, self.v, self.mask = (slab(g[x]) for x in ("q", "k", "v", "mask"))
+        self.out = torch.zeros((self.R, n, w.n_tok, w.n_head, w.hd), dtype=torch.float32,
+                               device=dev)
+        self.bytes = per * self.R
+
+
+def make_call(F, w, pool, flags):
+    fmt = F.FR_Q_F16 if w.q_dtype == "f16" else F.FR_Q_F32
+    M = w.M
+    lib = F.binding.load()
+    qs, ks, ms, os_ = M * w.hd, w.n_kv * w.hd, w.n_tok * w.n_kv, M * w.hd
+    ptrs = [(pool.q[r].data_ptr(), pool.k[r].data_ptr(), pool.v[r].data_ptr(),
+             pool.mask[r].data_ptr(), pool.out[r].data_ptr()) for r in range(pool.R)]
+
+    def call(slot, stream):
+        q, k, v, m, o = ptrs[slot]
+        st = lib.fr_decode_attn_ex(q, fmt, k, v, m, o, w.n_inst, qs, ks, ms, os_, w.n_head,
+                                   w.n_tok, w.n_kv, w.hd, w.scale, flags, None, 0, stream)
+        if st != 0:
+            raise F.FrError(st, "fr_decode_attn_ex")
+
+    return call
+
+
+def sleep_cycles_for(torch, ms: float) -> int:
+    """Calibrate torch.cuda._sleep (a bounded spin kernel) to about `ms`."""
+    cycles = 1_000_000
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(cycles)
+    e1.record()
+    torch.cuda.synchronize()
+    per_ms = cycles / max(e0.elapsed_time(e1), 1e-3)
+    return int(per_ms * ms)
+
+
+def timed_region(torch, F, call, R, steps, stream_handle, same_slot=False):
+    """K calls queued behind a GPU sleep; returns (ms per call, main-kernel ms list)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in starts + stops:   # instantiate the underlying hipEvents
+        e.record()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    # host enqueue rate, to size the sleep that keeps the queue ahead of the GPU
+    h0 = time.perf_counter()
+    for i in range(min(steps, 20)):
+        call(0 if same_slot else i % R, stream_handle)
+    torch.cuda.synchronize()
+    host_per_call = (time.perf_counter() - h0) / min(steps, 20)
+    cycles = sleep_cycles_for(torch, max(20.0, 3.0 * host_per_call * 1e3 * steps))
+
+    torch.cuda.synchronize()
+    torch.cuda._sleep(cycles)
+    t0.record()
+    for i in range(steps):
+        F.fr_decode_attn_profile_events(starts[i].cuda_event, stops[i].cuda_event)
+        call(0 if same_slot else i % R, stream_handle)
+    F.fr_decode_attn_profile_events(None, None)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    kern = [a.elapsed_time(b) for a, b in zip(starts, stops)]
+    return ms_total / steps, kern
+
+
+def traffic_for(w_name: str, variant: int):
+    """HBM bytes per main-kernel launch from the committed rocprofv3 counter
+    summary, or None if missing or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    rec = t.get("workloads", {}).get(w_name)
+    if not rec or rec.get("variant") != variant:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, g, gpu_out, repeats):
+    import oracle
+    q_kind = oracle.Q_F16 if w.q_dtype == "f16" else oracle.Q_F32
+    times, threads = [], 0
+    out = None
+    for _ in range(max(1, repeats)):
+        t = time.perf_counter()
+        res = []
+        for i in range(w.n_inst):
+            o, threads = oracle.decode_attn(g["q"][i], g["k"][i], g["v"][i], g["mask"][i],
+                                            w.n_head, w.n_tok, w.n_kv, w.hd, w.scale,
+                                            q_kind=q_kind, return_threads=True)
+            res.append(o)
+        times.append(time.perf_counter() - t)
+        out = np.stack(res)
+    med = statistics.median(times)
+    err = float(np.max(np.abs(out - gpu_out.astype(np.float64))))
+    return {"value": round(med * 1e6, 1), "unit": "us/call", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"the full {w.n_inst}-instance batch of the timed workload, "
+                      f"median of {len(times)} fp64 runs",
+            "max_abs_vs_gpu": err}
+
+
+def run_workload(args, torch, F, W, w):
+    flags = {"auto": 0, "fused": F.FR_VARIANT_FUSED,
+             "decomposed": F.FR_VARIANT_DECOMPOSED}[args.variant]
+    if args.round_f16:
+        flags |= F.FR_Q_ROUND_F16
+    plan = F.fr_decode_attn_plan(w.n_inst, w.n_head, w.n_tok, w.n_kv, w.hd, flags)
+    g = W.generate(w)
+    pool = Pool(torch, w, g, args.pool_gib * (1 << 30))
+    F.fr_decode_attn_reserve(w.n_inst, w.n_head, w.n_tok, w.n_kv, w.hd, flags)
+    call = make_call(F, w, pool, flags)
+    stream = int(torch.cuda.current_stream().cuda_stream)
+
+    for i in range(args.warmup):
+        call(i % pool.R, stream)
+    torch.cuda.synchronize()
+    # every slot holds the same inputs, so every slot's output must be identical
+    outs = pool.out[: min(pool.R, max(args.warmup, 1))]
+    if not bool(torch.isfinite(outs).all()) or not bool((outs == outs[0]).all()):
+        raise RuntimeError("warm-up outputs differ across pool slots or are not finite")
+    gpu_out = pool.out[0].cpu().numpy()
+
+    ms_call, kern = timed_region(torch, F, call, pool.R, args.steps, stream)
+    kern_ms = statistics.mean(kern)
+    alg = w.algorithmic_bytes()
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    call_gbs = alg / (ms_call * 1e-3) / 1e9
+    aux = {
+        "us_per_instance": round(ms_call * 1e3 / w.n_inst, 3),
+        "call_GBps": round(call_gbs, 1),
+        "call_frac_of_hbm_peak": round(call_gbs / PEAK_HBM_GBS, 4),
+        "main_kernel_us_mean": round(kern_ms * 1e3, 3),
+        "main_kernel_us_median": round(statistics.median(kern) * 1e3, 3),
+        "mfma_frac_of_f16_peak": round(w.flops() / (kern_ms * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS,
+                                       4),
+        "plan": plan,
+        "pool_copies": pool.R,
+        "pool_GiB": round(pool.bytes / (1 << 30), 3),
+        "algorithmic_bytes": alg,
+        "flops": w.flops(),
+    }
+    if args.warm:
+        ms_warm, kern_warm = timed_region(torch, F, call, pool.R, args.steps, stream,
+                                          same_slot=True)
+        aux["warm_cache_resident_us_per_call"] = round(ms_warm * 1e3, 3)
+        aux["warm_cache_resident_kernel_us"] = round(statistics.mean(kern_warm) * 1e3, 3)
+
+    traffic = traffic_for(w.name, plan["variant"])
+    rec = {
+        "metric": METRIC,
+        "value": round(ms_call * 1e3, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_call, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 mfma, fp32 accumulate/softmax" + (
+            " (f32 Q as hi+lo f16)" if w.q_dtype == "f32" and not args.round_f16 else ""),
+        "data": "synthetic (seeded normal Q/K/V, f16 0/-inf masks; no checkpoint)",
+        "config": {"workload": w.name, "n_inst": w.n_inst, "n_head": w.n_head,
+                   "n_tok": w.n_tok, "n_kv": w.n_kv, "n_valid": w.n_valid, "hd": w.hd,
+                   "q_dtype": w.q_dtype, "variant": args.variant,
+                   "round_f16": bool(args.round_f16)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+        "aux": aux,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, g, gpu_out, args.cpu_repeats)
+    del pool
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (independent instances or KV shards would each run this kernel on "
+              "their own GPU).", file=sys.stderr)
+        return 2
+    import torch
+
+    import gqa_decode_attention_fr_amd as F
+    from gqa_decode_attention_fr_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    F.binding.load()
+    names = [w.name for w in W.WORKLOADS] if args.workload == "all" else [args.workload]
+    for name in names:
+        if name not in W.BY_NAME:
+            print(f"unknown workload {name}; choose from {list(W.BY_NAME)}", file=sys.stderr)
+            return 1
+        rec = run_workload(args, torch, F, W, W.BY_NAME[name])
+        print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

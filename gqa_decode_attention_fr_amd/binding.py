@@ -31,7 +31,8 @@ FR_VARIANT_DECOMPOSED = 0x4
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
             "fr_decode_attn_ex", "fr_decode_attn_workspace_size", "fr_decode_attn_reserve",
-            "fr_decode_attn_plan", "fr_status_str", "fr_abi_version")
+            "fr_decode_attn_plan", "fr_decode_attn_profile_events", "fr_status_str",
+            "fr_abi_version")
 
 PLAN_FIELDS = ("variant", "n_split", "chunk", "waves", "tiles", "n_rowblk", "grid", "launches")
 
@@ -53,6 +54,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is missing: build it with `python -m gqa_decode_attention_fr_amd.build`")
+    try:  # load torch's HIP runtime first so that torch and the library share one
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32, u32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                   ctypes.c_float, ctypes.c_uint, ctypes.c_size_t)
@@ -71,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fr_decode_attn_workspace_size.restype = sz
     lib.fr_decode_attn_reserve.argtypes = [i32, i32, i32, i32, i32, u32]
     lib.fr_decode_attn_plan.argtypes = [i32, i32, i32, i32, i32, u32, ctypes.POINTER(i32), i32]
+    lib.fr_decode_attn_profile_events.argtypes = [vp, vp]
+    lib.fr_decode_attn_profile_events.restype = i32
     lib.fr_status_str.argtypes = [i32]
     lib.fr_status_str.restype = ctypes.c_char_p
     lib.fr_abi_version.argtypes = []
@@ -155,6 +162,11 @@ def fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> dict:
     _check(load().fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags, info,
                                       len(PLAN_FIELDS)), "fr_decode_attn_plan")
     return dict(zip(PLAN_FIELDS, list(info)))
+
+
+def fr_decode_attn_profile_events(start, stop) -> None:
+    """start/stop: raw hipEvent_t handles (ints) or None, None to turn timing off."""
+    _check(load().fr_decode_attn_profile_events(start, stop), "fr_decode_attn_profile_events")
 
 
 def fr_status_str(status: int) -> str:

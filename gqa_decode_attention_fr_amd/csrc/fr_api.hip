@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -21,7 +22,7 @@
 
 namespace fr {
 
-int tiles_per_wave(int hd);
+int max_tiles_per_wave(int hd, bool f16_query);  // fused split kernel register budget
 
 int env_int(const char *name, int fallback) {
   const char *s = std::getenv(name);
@@ -31,22 +32,46 @@ int env_int(const char *name, int fallback) {
 
 bool debug_on() { return env_int("FR_DEBUG", 0) != 0; }
 
+static std::atomic<hipEvent_t> g_prof_start{nullptr};
+static std::atomic<hipEvent_t> g_prof_stop{nullptr};
+
+void profile_events(hipEvent_t *start, hipEvent_t *stop) {
+  *start = g_prof_start.load();
+  *stop = g_prof_stop.load();
+  if (!*start || !*stop) *start = *stop = nullptr;
+}
+
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Workgroups the split kernel should launch to cover the machine: 256 compute
 // units on MI355X, one resident workgroup per unit at these LDS sizes.
 constexpr int kTargetWorkgroups = 256;
 
-int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flags, Plan *plan) {
+int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flags,
+              bool f16_query, Plan *plan) {
   Plan p;
   const int M = n_head * n_tok;
   p.variant = (flags & FR_VARIANT_DECOMPOSED) ? kDecomposed : kFused;
-  const int tiles = tiles_per_wave(hd);
   const int tiles_total = (int)cdiv(M, 16);
-  const int waves_needed = (int)cdiv(tiles_total, tiles);
-  p.tiles = tiles;
-  // fused: 4..8 waves share each LDS block; decomposed kernels use 4 waves
-  p.waves = p.variant == kDecomposed ? 4 : std::min(8, std::max(4, waves_needed));
+  if (p.variant == kDecomposed) {
+    // QK^T and PV kernels: 4 waves, a fixed number of 16-row tiles per wave
+    p.waves = 4;
+    p.tiles = hd == 256 ? 1 : (hd == 128 ? 2 : 4);
+  } else {
+    // split kernel: up to 4 tiles run as 4 waves x 1 tile (one wave per SIMD);
+    // larger row counts use 8 waves (two per SIMD, hiding each other's
+    // latency) with as many tiles per wave as the register budget allows
+    if (tiles_total <= 4) {
+      p.waves = 4;
+      p.tiles = 1;
+    } else {
+      p.waves = 8;
+      p.tiles = 1;
+      const int cap = max_tiles_per_wave(hd, f16_query);
+      while (p.tiles < cap && p.waves * p.tiles < tiles_total) p.tiles *= 2;
+    }
+  }
+  const int tiles = p.tiles;
   const int rows_per_wg = p.waves * tiles * 16;
   p.n_rowblk = (int)cdiv(M, rows_per_wg);
   const int key_blocks = (int)cdiv(n_kv, kKeyBlock);
@@ -207,7 +232,8 @@ int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const
   if (st != FR_OK) return st;
   if (n_inst == 1) q_stride = kv_stride = mask_stride = out_stride = 0;
   Plan plan;
-  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &plan);
+  const bool f16_query = q_format == FR_Q_F16 || (flags & FR_Q_ROUND_F16);
+  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, f16_query, &plan);
   if (st != FR_OK) return st;
   if (caller_ws) {
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
@@ -285,11 +311,21 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k, const uint
 size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv, int hd,
                                      unsigned flags, int *status) {
   int st = check_sizes(n_inst, n_head, n_tok, n_kv, hd);
-  if (st == FR_OK) st = check_flags(FR_Q_F32, flags & ~FR_Q_ROUND_F16);
-  Plan plan;
-  if (st == FR_OK) st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &plan);
+  if (st == FR_OK) st = check_flags(FR_Q_F32, flags);
+  size_t need = 0;
+  if (st == FR_OK) {
+    // the plan depends on the query precision; cover f16 queries too unless
+    // the flags already say the query is used at f16 precision
+    Plan a, b;
+    st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, true, &a);
+    if (st == FR_OK && !(flags & FR_Q_ROUND_F16))
+      st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, false, &b);
+    else
+      b = a;
+    need = std::max(a.ws_bytes, b.ws_bytes);
+  }
   if (status) *status = st;
-  return st == FR_OK ? plan.ws_bytes : 0;
+  return st == FR_OK ? need : 0;
 }
 
 int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
@@ -305,14 +341,21 @@ int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, uns
                         int *info, int n_info) {
   if (!info || n_info < 0) return FR_ERR_INVALID;
   int st = check_sizes(n_inst, n_head, n_tok, n_kv, hd);
-  if (st == FR_OK) st = check_flags(FR_Q_F32, flags & ~FR_Q_ROUND_F16);
+  if (st == FR_OK) st = check_flags(FR_Q_F32, flags);
   if (st != FR_OK) return st;
   Plan p;
-  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &p);
+  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, (flags & FR_Q_ROUND_F16) != 0, &p);
   if (st != FR_OK) return st;
   const int vals[8] = {p.variant, p.n_split, p.chunk, p.waves,
                        p.tiles,   p.n_rowblk, p.grid, p.launches};
   for (int i = 0; i < n_info && i < 8; ++i) info[i] = vals[i];
+  return FR_OK;
+}
+
+int fr_decode_attn_profile_events(void *start, void *stop) {
+  if ((start == nullptr) != (stop == nullptr)) return FR_ERR_INVALID;
+  fr::g_prof_start.store((hipEvent_t)start);
+  fr::g_prof_stop.store((hipEvent_t)stop);
   return FR_OK;
 }
 

@@ -24,9 +24,6 @@
 #include "fr_internal.h"
 
 namespace fr {
-
-int tiles_per_wave(int hd);
-
 namespace {
 
 constexpr int kWaves = 4;
@@ -326,6 +323,9 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   qa.n_rowblk = plan.n_rowblk;
   qa.n_kblk = n_kblk;
   qa.scale = p.scale;
+  hipEvent_t ev0, ev1;
+  profile_events(&ev0, &ev1);
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
   const dim3 qgrid(p.n_inst * plan.n_rowblk * n_kblk);
   switch (p.hd) {
     case 64: launch_qk<64>(p.qmode, qgrid, stream, qa); break;
@@ -371,7 +371,8 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
     case 256: launch_pv<256>(pgrid, stream, pa); break;
   }
   err = hipGetLastError();
-  if (err != hipSuccess || plan.n_split == 1) return err;
+  if (err != hipSuccess) return err;
+  if (plan.n_split == 1) return ev1 ? hipEventRecord(ev1, stream) : hipSuccess;
 
   SumArgs ua;
   ua.part = part;
@@ -384,7 +385,9 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   const int64_t threads = (int64_t)p.n_inst * M * (p.hd / 4);
   hipLaunchKernelGGL(sum_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                      ua);
-  return hipGetLastError();
+  err = hipGetLastError();
+  if (err == hipSuccess && ev1) err = hipEventRecord(ev1, stream);
+  return err;
 }
 
 }  // namespace fr

@@ -8,43 +8,49 @@
 // over all n_head*n_tok query rows ordered t-major (row r = t*n_head + h), so
 // that row r's output is the contiguous slice out[r*hd .. r*hd + hd).
 //
-// The pages run the three steps as separate GEMM launches on Thor.  Here the
-// three steps run inside one kernel per key split, so the score matrix never
-// leaves the chip:
+// The pages run the three steps as separate GEMM launches on Thor.  Here they
+// run inside one kernel per key split, so scores and probabilities never
+// leave the chip:
 //
-//   workgroup = (instance, row block, key split)
-//     for each 64-key block of the split:
-//       K block  -> LDS as [key][d]           (16-byte coalesced loads)
-//       V block  -> LDS transposed [d][key]    (so PV's key-reduction operand is
-//                                               contiguous per lane)
-//       mask     -> LDS as fp32, pre-multiplied by log2(e); keys past n_kv = -inf
-//       each wave, for its 16-row tiles:
-//         S^T = K . Q^T        v_mfma_f32_16x16x32_f16, fp32 accumulation
-//                              (f32 Q enters as hi + lo f16 halves)
-//         online softmax       block max across the 4 lane groups of a row by
-//                              cross-lane shuffles, exp2 in fp32
-//         O^T += V^T . P^T     v_mfma_f32_16x16x32_f16 with unnormalised f16 P
-//     n_split == 1: out = O / l written directly
-//     n_split  > 1: (O, m, l) partials; a combine kernel merges them in a fixed
-//                   split order (deterministic)
+//   workgroup = 4 waves = (instance, row block, key split)
+//   K, V and mask blocks of 64 keys stream global -> LDS with gfx950's 16-byte
+//   direct-to-LDS loads (no register staging) into a two-stage ring, so block
+//   b+1 is in flight while block b is computed.  Waits are explicit vmcnt
+//   counts ahead of a plain s_barrier.
+//   each wave, for its 16-row tiles (tile i of wave w is tile w + 4i):
+//     S^T = K . Q^T       v_mfma_f32_16x16x32_f16, fp32 accumulation; an f32 Q
+//                         enters as hi + lo f16 halves (two MFMAs)
+//     online softmax      scale*log2(e) folded in, exp2, block max shared by
+//                         the four lane groups of a row through two shuffles
+//     O^T += V^T . P^T    V^T operand read with ds_read_b64_tr_b16 straight
+//                         from V's natural [key][d] layout; P is unnormalised f16
+//   n_split == 1: out = O / l;  n_split > 1: (O, m, l) partials merged by the
+//   combine kernel in split order (deterministic).
 //
-// MFMA operand mapping used throughout (16x16 tiles, wave64): the A operand
-// lane L supplies row (L % 16), the B operand lane L supplies column (L % 16),
-// both with 8 contraction elements per lane indexed by (L / 16, element); the
-// accumulator lane L holds rows 4*(L/16) .. +3 of column (L % 16).  Because
-// K (or V^T) is the A operand and Q (or P) the B operand, every lane owns one
-// query row (L % 16) in both the score and the output accumulators, so the
-// softmax statistics and the output rescaling stay lane-local.
+// MFMA operand mapping (16x16 tiles, wave64): A-operand lane L supplies row
+// L%16, B-operand lane L column L%16, each with 8 contraction elements indexed
+// by (L/16, element); accumulator lane L holds rows 4*(L/16)..+3 of column
+// L%16.  K (or V^T) is the A operand and Q (or P) the B operand, so a lane owns
+// one query row in both accumulators and the softmax state stays lane-local.
+//
+// LDS layouts are unpadded and XOR-swizzled at 16-byte granularity: granule c
+// of row r sits in slot c ^ swz(r).  The K swizzle makes the 16 rows of one
+// score-tile read hit distinct banks; the V swizzle does the same for the four
+// rows each 16-lane group touches in a transposing read.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <utility>
 
 #include "fr_device.h"
 #include "fr_internal.h"
 
 namespace fr {
 namespace {
+
+enum MaskMode { kMaskNone = 0, kMaskDma = 1, kMaskReg = 2 };
 
 struct SplitArgs {
   const void *q;
@@ -57,24 +63,140 @@ struct SplitArgs {
   int64_t q_stride, kv_stride, mask_stride, out_stride;
   int n_head, n_tok, n_kv, M;
   int n_split, chunk, n_rowblk;
-  float scale_log2; // scale * log2(e)
+  float scale;      // applied to q.k before the mask
 };
 
-template <int HD, int WAVES, int TILES, int QMODE>
-__global__ __launch_bounds__(WAVES * 64) void split_kernel(SplitArgs a) {
-  constexpr int NT = WAVES * 64;
-  constexpr int KSTR = HD + 8;   // halfs per K row in LDS (pad spreads banks)
-  constexpr int VSTR = KB + 8;   // halfs per V^T row in LDS
-  constexpr int GPR = HD / 8;    // 16-byte granules per K/V row
-  constexpr int NK = (KB * GPR + NT - 1) / NT;
-  constexpr int NV = ((KB / 4) * GPR + NT - 1) / NT;
-  constexpr int NMASK = (kMaxTok * KB + NT - 1) / NT;
-  constexpr int KS = HD / 32;    // contraction steps of QK^T
-  constexpr int DT = HD / 16;    // 16-wide d tiles of the output
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
 
-  __shared__ __attribute__((aligned(16))) _Float16 sK[KB * KSTR];
-  __shared__ __attribute__((aligned(16))) _Float16 sVt[HD * VSTR];
-  __shared__ __attribute__((aligned(16))) float sM[kMaxTok * KB];
+__device__ __forceinline__ int swz_k(int r, int gpr) {
+  return ((r & 3) | (((r >> 3) & 3) << 2)) & (gpr - 1);
+}
+__device__ __forceinline__ int swz_v(int r, int gpr) {
+  return ((2 * (r & 3)) | (((r >> 3) & 1) << 3)) & (gpr - 1);
+}
+__device__ __forceinline__ int swz_m(int t) { return t & 7; }
+
+// 16-byte global -> LDS copy: lane l's bytes land at lds_base + 16*l.
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((global_cvoid *)g, (lds_void *)lds_base, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS accesses in the compiler without waiting
+// on outstanding direct-to-LDS loads (the waits above cover those).
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ half4 lds_tr16(const _Float16 *p) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4;
+  fp16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (__attribute__((address_space(3))) fp16x4 *)(p));
+  return __builtin_bit_cast(half4, v);
+}
+
+// Lazy softmax reference: the running max moves only when a block's max is
+// more than 8*ln(2) above it, so unnormalised probabilities stay <= 2^8.
+constexpr float kLazy = 5.545177444479562f;
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four lane groups
+// that share one query row) with gfx950's VALU row swaps, no LDS traffic:
+// after a self-swap, the two results of a lane hold its own value and its
+// partner's (partner = l^32, then l^16).
+__device__ __forceinline__ float group_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---- LDS reads of the compute phase, issued as inline assembly.  The
+// compiler would otherwise wait for every outstanding direct-to-LDS load
+// (including the next block's prefetch) before the first read of a block; the
+// explicit vmcnt waits ahead of each barrier already order those loads.  The
+// reads complete in issue order, and every consumer waits with lgkmcnt(N) on
+// the fragments it uses (tied through the wait, so it cannot move above it).
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+template <int OFF>
+__device__ __forceinline__ half8 lds_b128(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  half8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ uint2v lds_tr_b64(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  uint2v r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+}
+template <int N, typename T>
+__device__ __forceinline__ void wait_lgkm_tie(T &x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+template <int N, typename T>
+__device__ __forceinline__ void wait_lgkm_tie(T &x, T &y) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
+}
+template <int N, typename T>
+__device__ __forceinline__ void wait_lgkm_tie(T &x, T &y, T &z, T &w) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x), "+v"(y), "+v"(z), "+v"(w) : "i"(N));
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int HD, int NW>
+struct Stage {
+  _Float16 k[KB * HD];
+  _Float16 v[KB * HD];
+  uint16_t m[NW * 64 * 8];  // one 16-byte granule per lane; 16 tokens x 8 are read
+};
+
+// NW waves per workgroup (4 or 8), TPW 16-row tiles per wave.
+template <int HD, int NW, int TPW, int QMODE, int MASKMODE>
+__global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
+  constexpr int kWaves = NW;
+  constexpr int kThreads = NW * 64;
+  constexpr int GPR = HD / 8;                 // 16-byte granules per K/V row
+  constexpr int NJ = GPR / NW;                // K (and V) DMA instructions per wave per block
+  constexpr int NMR = (kMaxTok * KB) / kThreads; // register-path mask loads per thread
+  constexpr int NJM = MASKMODE == kMaskDma ? 1 : (MASKMODE == kMaskReg ? NMR : 0);
+  static_assert(NJ >= 1 && NJ * NW == GPR, "K/V rows split evenly over the waves");
+  constexpr int J = 2 * NJ + NJM;             // vector-memory ops per wave per block
+  constexpr int KS = HD / 32;
+  constexpr int DT = HD / 16;
+
+  __shared__ __attribute__((aligned(16))) Stage<HD, NW> st0;
+  __shared__ __attribute__((aligned(16))) Stage<HD, NW> st1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -95,203 +217,331 @@ __global__ __launch_bounds__(WAVES * 64) void split_kernel(SplitArgs a) {
   const int key_end = min(key_begin + a.chunk, a.n_kv);
   const int nblk = (key_end - key_begin + KB - 1) / KB;
 
-  // ---- staging registers for the next block (global -> VGPR -> LDS)
-  uint4v rk[NK];
-  uint4v rv[NV][4];
-  uint16_t rm[NMASK];
+  uint16_t rm[2][NMR]; // register-staged mask values (kMaskReg only)
 
-  auto load_block = [&](int kb0) {
+  // Issue every load of one 64-key block into stage `s`.
+  auto issue = [&](Stage<HD, NW> &s, int kb0, uint16_t (&rmr)[NMR]) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int u = tid + i * NT;
-      const int row = u / GPR, c = u % GPR;
-      const int key = kb0 + row;
-      uint4v val = {0u, 0u, 0u, 0u};
-      if (u < KB * GPR && key < key_end)
-        val = *(const uint4v *)(kbase + (int64_t)key * HD + c * 8);
-      rk[i] = val;
+    for (int j = 0; j < NJ; ++j) {
+      const int lin = (wave * NJ + j) * 64 + lane;   // granule index in the block
+      const int r = lin / GPR, slot = lin % GPR;
+      const int key = min(kb0 + r, a.n_kv - 1);      // rows past n_kv: any valid row
+      dma16(kbase + (int64_t)key * HD + 8 * (slot ^ swz_k(r, GPR)),
+            (char *)s.k + (wave * NJ + j) * 1024);
+      dma16(vbase + (int64_t)key * HD + 8 * (slot ^ swz_v(r, GPR)),
+            (char *)s.v + (wave * NJ + j) * 1024);
     }
+    if (MASKMODE == kMaskDma) {
+      const int lin = wave * 64 + lane;              // one granule per lane; 128 are read
+      const int t = lin >> 3, gr = (lin & 7) ^ swz_m(lin >> 3);
+      const bool ok = t < a.n_tok && kb0 + 8 * gr < a.n_kv;
+      const uint16_t *src = ok ? mbase + (int64_t)t * a.n_kv + kb0 + 8 * gr : mbase;
+      dma16(src, (char *)s.m + wave * 1024);
+    } else if (MASKMODE == kMaskReg) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int u = tid + i * NT;
-      const int kq = u / GPR, c = u % GPR;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kb0 + 4 * kq + e;
-        uint4v val = {0u, 0u, 0u, 0u};
-        if (u < (KB / 4) * GPR && key < key_end)
-          val = *(const uint4v *)(vbase + (int64_t)key * HD + c * 8);
-        rv[i][e] = val;
+      for (int i = 0; i < NMR; ++i) {
+        const int u = tid + i * kThreads;            // 1024 = 16 tokens x 64 keys
+        const int t = u >> 6, j = u & 63;
+        const bool ok = t < a.n_tok && kb0 + j < a.n_kv;
+        rmr[i] = mbase[ok ? (int64_t)t * a.n_kv + kb0 + j : 0];
       }
-    }
-#pragma unroll
-    for (int i = 0; i < NMASK; ++i) {
-      const int u = tid + i * NT;
-      const int t = u / KB, j = u % KB;
-      const int key = kb0 + j;
-      uint16_t mv = 0xFC00; // -inf: keys outside this split or past n_kv
-      if (key < key_end) mv = (mbase && t < a.n_tok) ? mbase[(int64_t)t * a.n_kv + key] : 0;
-      rm[i] = mv;
     }
   };
 
-  auto store_block = [&]() {
+  // kMaskReg: place the register-staged values (after they have arrived).
+  auto place_mask = [&](Stage<HD, NW> &s, const uint16_t (&rmr)[NMR]) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int u = tid + i * NT;
-      if (u < KB * GPR) {
-        const int row = u / GPR, c = u % GPR;
-        *(uint4v *)(sK + row * KSTR + c * 8) = rk[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int u = tid + i * NT;
-      if (u < (KB / 4) * GPR) {
-        const int kq = u / GPR, c = u % GPR;
-        // rv[i][e] holds V[4kq+e][8c .. 8c+7]; write V^T rows d = 8c+dd with
-        // the four keys 4kq .. 4kq+3 packed in one 8-byte store.
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t k0 = rv[i][0][w], k1 = rv[i][1][w];
-          const uint32_t k2 = rv[i][2][w], k3 = rv[i][3][w];
-          const uint32_t lo01 = (k0 & 0xFFFFu) | (k1 << 16);
-          const uint32_t lo23 = (k2 & 0xFFFFu) | (k3 << 16);
-          const uint32_t hi01 = (k0 >> 16) | (k1 & 0xFFFF0000u);
-          const uint32_t hi23 = (k2 >> 16) | (k3 & 0xFFFF0000u);
-          typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
-          *(uint2v *)(sVt + (8 * c + 2 * w) * VSTR + 4 * kq) = uint2v{lo01, lo23};
-          *(uint2v *)(sVt + (8 * c + 2 * w + 1) * VSTR + 4 * kq) = uint2v{hi01, hi23};
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NMASK; ++i) {
-      const int u = tid + i * NT;
-      if (u < kMaxTok * KB) sM[u] = (float)bits_to_half(rm[i]) * kLog2e;
+    for (int i = 0; i < NMR; ++i) {
+      const int u = tid + i * kThreads;
+      const int t = u >> 6, j = u & 63;
+      s.m[(t * 8 + ((j >> 3) ^ swz_m(t))) * 8 + (j & 7)] = rmr[i];
     }
   };
 
-  // ---- this wave's query rows: tiles of 16, lane owns row l16 of each tile
-  const int tile0 = rowblk * (WAVES * TILES) + wave * TILES;
-  const bool wave_active = tile0 * 16 < a.M;
-
-  load_block(key_begin);
-
-  half8 qh[TILES][KS], ql[TILES][KS];
-  int tok[TILES];
+  // ---- query rows of this wave: tile i is tile (wave + 4i) of the row block
+  const int tile_base = rowblk * (kWaves * TPW) + wave;
+  // a wave with no row in range skips the arithmetic (it still loads and
+  // joins every barrier); inside a wave all TPW tiles are computed, rows past
+  // M carry zero queries and are never stored
+  const bool wave_on = tile_base * 16 < a.M;
+  int tok[TPW];
+  // raw query values first; they are split into f16 operands only after the
+  // first block has landed, so waiting on them never waits on the prefetch
+  float4v qraw[TPW][KS][2];
   const void *qinst = (QMODE == kQF16)
                           ? (const void *)((const uint16_t *)a.q + (int64_t)inst * a.q_stride)
                           : (const void *)((const float *)a.q + (int64_t)inst * a.q_stride);
 #pragma unroll
-  for (int i = 0; i < TILES; ++i) {
-    const int r = (tile0 + i) * 16 + l16;
-    const bool rvalid = r < a.M;
+  for (int i = 0; i < TPW; ++i) {
+    const int tile = tile_base + kWaves * i;
+    const int r = tile * 16 + l16;
     tok[i] = min(r / a.n_head, a.n_tok - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      load_q8<QMODE>(qinst, (int64_t)r * HD + ks * 32 + g * 8, rvalid, qh[i][ks], ql[i][ks]);
-  }
-
-  float m_run[TILES], l_run[TILES];
-  float4v o[TILES][DT];
-#pragma unroll
-  for (int i = 0; i < TILES; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[i][dt] = float4v{0.f, 0.f, 0.f, 0.f};
-  }
-
-  for (int b = 0; b < nblk; ++b) {
-    if (b > 0) __syncthreads(); // every wave is done reading the previous block
-    store_block();
-    __syncthreads();
-    if (b + 1 < nblk) load_block(key_begin + (b + 1) * KB); // in flight during compute
-
-    if (wave_active) {
-      // -- S^T = K . Q^T for the four 16-key tiles kt of this block.  Tile kt
-      //    feeds K rows so that lane group g ends up holding keys
-      //    32*(kt/2) + 8g + 4*(kt%2) + 0..3: the 8 keys of group g per 32-key
-      //    half are then contiguous, matching PV's contraction layout.
-      float4v s[TILES][4];
-#pragma unroll
-      for (int i = 0; i < TILES; ++i)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) s[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const int krow = (kt >> 1) * 32 + (l16 >> 2) * 8 + (kt & 1) * 4 + (l16 & 3);
-          const half8 kf = *(const half8 *)(sK + krow * KSTR + ks * 32 + g * 8);
-#pragma unroll
-          for (int i = 0; i < TILES; ++i) {
-            s[i][kt] = mfma16x16x32(kf, qh[i][ks], s[i][kt]);
-            if (QMODE == kQHiLo) s[i][kt] = mfma16x16x32(kf, ql[i][ks], s[i][kt]);
-          }
+    for (int ks = 0; ks < KS; ++ks) {
+      const int64_t off = (int64_t)r * HD + ks * 32 + g * 8;
+      float4v x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+      if (r < a.M) {
+        if (QMODE == kQF16) {
+          x0 = __builtin_bit_cast(float4v, *(const uint4v *)((const uint16_t *)qinst + off));
+        } else {
+          x0 = *(const float4v *)((const float *)qinst + off);
+          x1 = *(const float4v *)((const float *)qinst + off + 4);
         }
       }
+      qraw[i][ks][0] = x0;
+      qraw[i][ks][1] = x1;
+    }
+  }
+  asm volatile("" ::: "memory"); // query loads are issued before the block loads
 
-      // -- scale, mask, online softmax; pack P^T as the PV B operand
-      half8 pb[TILES][2];
-#pragma unroll
-      for (int i = 0; i < TILES; ++i) {
-        const float *mrow = sM + tok[i] * KB;
-        float x[16];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const float4v m0 = *(const float4v *)(mrow + 32 * hh + 8 * g);
-          const float4v m1 = *(const float4v *)(mrow + 32 * hh + 8 * g + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[8 * hh + e] = s[i][2 * hh][e] * a.scale_log2 + m0[e];
-            x[8 * hh + 4 + e] = s[i][2 * hh + 1][e] * a.scale_log2 + m1[e];
-          }
-        }
-        float bm = x[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) bm = fmaxf(bm, x[e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float m_new = fmaxf(m_run[i], bm);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[i] - m_use);
-        m_run[i] = m_new;
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(x[e] - m_use);
-          psum += p;
-          pb[i][e >> 3][e & 7] = (_Float16)p;
-        }
-        l_run[i] = l_run[i] * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[i][dt] *= alpha;
-      }
+  issue(st0, key_begin, rm[0]);
+  if (nblk > 1) {
+    issue(st1, key_begin + KB, rm[1]);
+    wait_vm<J>();
+  } else {
+    wait_vm<0>();
+  }
 
-      // -- O^T += V^T . P^T over the two 32-key halves of the block
+  half8 qh[TPW][KS], ql[TPW][KS];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+  for (int i = 0; i < TPW; ++i) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const half8 vf = *(const half8 *)(sVt + (dt * 16 + l16) * VSTR + 32 * hh + 8 * g);
+    for (int ks = 0; ks < KS; ++ks) {
+      float4v x0 = qraw[i][ks][0], x1 = qraw[i][ks][1];
+      asm volatile("" : "+v"(x0), "+v"(x1)); // keep the split after the wait above
+      if (QMODE == kQF16) {
+        qh[i][ks] = __builtin_bit_cast(half8, x0);
+        ql[i][ks] = half8{};
+      } else {
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-          for (int i = 0; i < TILES; ++i) o[i][dt] = mfma16x16x32(vf, pb[i][hh], o[i][dt]);
+        for (int e = 0; e < 8; ++e) {
+          const _Float16 h = (_Float16)x[e]; // round to nearest even
+          qh[i][ks][e] = h;
+          ql[i][ks][e] = (QMODE == kQHiLo) ? (_Float16)(x[e] - (float)h) : (_Float16)0.f;
         }
       }
     }
   }
 
-  if (!wave_active) return;
-
-  // ---- finish: full row sums, then either the final output or a partial
+  // m_run: reference max in natural-log units; lacc: running row sums (all four
+  // elements equal); o: unnormalised output tiles
+  float m_run[TPW], alpha[TPW];
+  float4v lacc[TPW];
+  float4v o[TPW][DT];
+  const half8 kOnes = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                       (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
 #pragma unroll
-  for (int i = 0; i < TILES; ++i) {
-    float l = l_run[i];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int r = (tile0 + i) * 16 + l16;
+  for (int i = 0; i < TPW; ++i) {
+    m_run[i] = -INFINITY;
+    alpha[i] = 1.f;
+    lacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[i][dt] = float4v{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- per-lane LDS byte offsets.  With the swizzles above, the XOR term of
+  // a K read depends on the lane and on ks mod 4 only, and that of a V read on
+  // the lane and dt mod 8 only; everything else is a compile-time immediate.
+  //   K row of score tile kt, lane q = l16:  32*(kt/2) + 4*(kt%2) + [8*(q/4) + q%4]
+  //   K slot of step ks: (4*ks + g) ^ swz_k(row) = 16*(ks/4) + ((4*(ks%4) + g) ^ (q % GPR))
+  //   V rows of a transposing read: 32*hh + 4*e + [8*g + q/4]
+  //   V slot of tile dt: 16*(dt/8) + ((2*(dt%8) + (q%4)/2) ^ swz_v(row)), swz_v lane-constant
+  constexpr int NKO = KS < 4 ? KS : 4;
+  constexpr int NVO = DT < 8 ? DT : 8;
+  int koff[NKO], voff[NVO];
+  {
+    const int krl = 8 * (l16 >> 2) + (l16 & 3);
+    const int qk = l16 & (GPR - 1);
+#pragma unroll
+    for (int j = 0; j < NKO; ++j) koff[j] = krl * HD * 2 + 16 * ((4 * j + g) ^ qk);
+    const int vrl = 8 * g + (l16 >> 2);
+    const int sv = swz_v(vrl, GPR);
+#pragma unroll
+    for (int j = 0; j < NVO; ++j)
+      voff[j] = vrl * HD * 2 + 16 * ((2 * j + ((l16 & 3) >> 1)) ^ sv) + 8 * (l16 & 1);
+  }
+
+  auto compute = [&](Stage<HD, NW> &s, int kb0) {
+    uint32_t kaddr[NKO], vaddr[NVO];
+#pragma unroll
+    for (int j = 0; j < NKO; ++j) kaddr[j] = lds_addr(s.k) + koff[j];
+#pragma unroll
+    for (int j = 0; j < NVO; ++j) vaddr[j] = lds_addr(s.v) + voff[j];
+
+    // mask values first, so their LDS latency hides behind the QK^T phase
+    half8 mh[TPW][2];
+    if (MASKMODE != kMaskNone) {
+      const uint32_t mb = lds_addr(s.m);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const uint32_t ma0 = mb + 16 * (tok[i] * 8 + ((0 + g) ^ swz_m(tok[i])));
+        const uint32_t ma1 = mb + 16 * (tok[i] * 8 + ((4 + g) ^ swz_m(tok[i])));
+        mh[i][0] = lds_b128<0>(ma0);
+        mh[i][1] = lds_b128<0>(ma1);
+      }
+    }
+
+    // -- S^T = K . Q^T for the four 16-key tiles kt of the block.  Tile kt feeds
+    //    K rows so that lane group g ends up holding keys 32*(kt/2) + 8g +
+    //    4*(kt%2) + 0..3: per 32-key half, group g owns 8 consecutive keys.
+    //    The four K fragments of step ks+1 are read before the MFMAs of step ks.
+    float4v sc[TPW][4];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sc[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
+    half8 kb[2][4];
+    auto kread = [&](auto KSI, half8 (&dst)[4]) {
+      constexpr int ks = decltype(KSI)::value;
+      static_for<4>([&](auto KTI) {
+        constexpr int kt = decltype(KTI)::value;
+        dst[kt] = lds_b128<256 * (ks >> 2) + (32 * (kt >> 1) + 4 * (kt & 1)) * HD * 2>(
+            kaddr[ks & 3]);
+      });
+    };
+    kread(std::integral_constant<int, 0>{}, kb[0]);
+    static_for<KS>([&](auto KSI) {
+      constexpr int ks = decltype(KSI)::value;
+      if constexpr (ks + 1 < KS) kread(std::integral_constant<int, ks + 1>{}, kb[(ks + 1) & 1]);
+      constexpr int pending = (ks + 1 < KS) ? 4 : 0;
+      wait_lgkm_tie<pending>(kb[ks & 1][0], kb[ks & 1][1], kb[ks & 1][2], kb[ks & 1][3]);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          sc[i][kt] = mfma16x16x32(kb[ks & 1][kt], qh[i][ks], sc[i][kt]);
+          if (QMODE == kQHiLo) sc[i][kt] = mfma16x16x32(kb[ks & 1][kt], ql[i][ks], sc[i][kt]);
+        }
+      }
+    });
+    // (the last wait above was lgkmcnt(0): the mask values have landed too)
+    if (MASKMODE != kMaskNone) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) wait_lgkm_tie<0>(mh[i][0], mh[i][1]);
+    }
+
+    // -- V^T operand reads for PV: each transposing read gives lane (q, g) the
+    //    4 keys 32hh+8g+4e+0..3 of column d = 16dt + q, the key order of P.
+    //    The first pair is issued now, ahead of the softmax arithmetic.
+    uint2v vr[2][2];
+    auto vread = [&](auto IDX, uint2v (&dst)[2]) {
+      constexpr int idx = decltype(IDX)::value;
+      constexpr int hh = idx / DT, dt = idx % DT;
+      constexpr int off = 256 * (dt >> 3) + 32 * hh * HD * 2;
+      dst[0] = lds_tr_b64<off>(vaddr[dt & 7]);
+      dst[1] = lds_tr_b64<off + 4 * HD * 2>(vaddr[dt & 7]);
+    };
+    vread(std::integral_constant<int, 0>{}, vr[0]);
+
+    // -- scale + mask (natural-log units), online softmax; pack P^T as the PV
+    //    B operand.  The reference max m_ref only moves when a block's max
+    //    exceeds it by more than kLazy (= 8 ln 2): exp(y - m_ref) then stays
+    //    at most 2^8, exact in f16, and the output rescale is almost never run.
+    const bool ragged = kb0 + KB > key_end;
+    half8 pb[TPW][2];
+    bool moved = false;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      float y[16];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float m0 = MASKMODE != kMaskNone ? (float)mh[i][hh][e] : 0.f;
+          const float m1 = MASKMODE != kMaskNone ? (float)mh[i][hh][4 + e] : 0.f;
+          y[8 * hh + e] = fmaf(sc[i][2 * hh][e], a.scale, m0);
+          y[8 * hh + 4 + e] = fmaf(sc[i][2 * hh + 1][e], a.scale, m1);
+        }
+      }
+      if (ragged) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb0 + 32 * (e >> 3) + 8 * g + (e & 7) >= key_end) y[e] = -INFINITY;
+      }
+      float bm = fmaxf(fmaxf(y[0], y[1]), y[2]);
+#pragma unroll
+      for (int e = 3; e < 16; e += 2) bm = fmaxf(fmaxf(bm, y[e]), e + 1 < 16 ? y[e + 1] : y[e]);
+      bm = group_max(bm);
+      const float m_old = m_run[i];
+      if (bm > m_old + kLazy) {     // also taken when m_old = -inf and bm is finite
+        alpha[i] = fast_exp2((m_old - bm) * kLog2e);   // 0 when m_old = -inf
+        m_run[i] = bm;
+        moved = true;
+      } else {
+        alpha[i] = 1.f;
+      }
+      const float nb = (m_run[i] == -INFINITY) ? 0.f : -m_run[i] * kLog2e;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        pb[i][e >> 3][e & 7] = (_Float16)fast_exp2(fmaf(y[e], kLog2e, nb));
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[i][dt] *= alpha[i];
+        lacc[i] *= alpha[i];
+      }
+    }
+
+    // -- O^T += V^T . P^T over the two 32-key halves, V fragments one step ahead
+    static_for<2 * DT>([&](auto IDX) {
+      constexpr int idx = decltype(IDX)::value;
+      constexpr int hh = idx / DT, dt = idx % DT;
+      if constexpr (idx + 1 < 2 * DT) vread(std::integral_constant<int, idx + 1>{}, vr[(idx + 1) & 1]);
+      constexpr int pending = (idx + 1 < 2 * DT) ? 2 : 0;
+      wait_lgkm_tie<pending>(vr[idx & 1][0], vr[idx & 1][1]);
+      const half4 v0 = __builtin_bit_cast(half4, vr[idx & 1][0]);
+      const half4 v1 = __builtin_bit_cast(half4, vr[idx & 1][1]);
+      const half8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) o[i][dt] = mfma16x16x32(vf, pb[i][hh], o[i][dt]);
+      if constexpr (dt == 0) {
+        // row sums of the f16 probabilities on the matrix core: an all-ones
+        // A operand puts sum_k P[k][row] in every element of lacc
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) lacc[i] = mfma16x16x32(kOnes, pb[i][hh], lacc[i]);
+      }
+    });
+  };
+
+  // ---- main loop: two blocks per trip, st0 then st1.  Invariant at the top
+  // of a trip: block b is complete in st0 and only block b+1 (into st1) may
+  // still be in flight, so reads of st0 never wait on the prefetch; the wait
+  // for the next block is taken at the point it is needed.
+  for (int b = 0; b < nblk; b += 2) {
+    if (MASKMODE == kMaskReg) {
+      place_mask(st0, rm[0]);
+      wait_lgkm<0>();
+    }
+    barrier();
+    if (wave_on) compute(st0, key_begin + b * KB);
+    barrier();
+    if (b + 2 < nblk) issue(st0, key_begin + (b + 2) * KB, rm[0]);
+    if (b + 1 >= nblk) break;
+    if (b + 2 < nblk) wait_vm<J>(); else wait_vm<0>();   // block b+1 landed
+    if (MASKMODE == kMaskReg) {
+      place_mask(st1, rm[1]);
+      wait_lgkm<0>();
+    }
+    barrier();
+    if (wave_on) compute(st1, key_begin + (b + 1) * KB);
+    barrier();
+    if (b + 3 < nblk) {
+      issue(st1, key_begin + (b + 3) * KB, rm[1]);
+      wait_vm<J>();                                       // block b+2 landed
+    } else {
+      wait_vm<0>();
+    }
+  }
+
+  // ---- finish: full row sums, then the final output or a partial
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (!wave_on) break;
+    const float l = lacc[i][0];
+    const int r = (tile_base + kWaves * i) * 16 + l16;
     if (r >= a.M) continue;
     if (a.n_split == 1) {
       const float inv = (l > 0.f) ? 1.f / l : 0.f;
@@ -303,7 +553,7 @@ __global__ __launch_bounds__(WAVES * 64) void split_kernel(SplitArgs a) {
       float *po = a.part_o + prow * HD;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) *(float4v *)(po + dt * 16 + 4 * g) = o[i][dt];
-      if (g == 0) a.part_ml[prow] = float2v{m_run[i], l};
+      if (g == 0) a.part_ml[prow] = float2v{m_run[i] * kLog2e, l};  // max in log2 units
     }
   }
 }
@@ -319,6 +569,7 @@ struct CombineArgs {
 // One thread per (instance, row, 4 consecutive d): merges the split partials in
 // split order.  out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, where m is
 // the largest m_s; a row with no visible key (m = -inf) is written as zeros.
+// Loops are unrolled so that each thread keeps several loads in flight.
 template <int HD>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int Q4 = HD / 4;
@@ -332,16 +583,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t base = (int64_t)inst * a.n_split;
 
   float m = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, a.part_ml[(base + s) * a.M + r].x);
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   if (m != -INFINITY) {
     float l = 0.f;
+#pragma unroll 8
     for (int s = 0; s < a.n_split; ++s) {
       const int64_t prow = (base + s) * a.M + r;
       const float2v ml = a.part_ml[prow];
+      const float4v po = *(const float4v *)(a.part_o + prow * HD + 4 * d4);
       const float w = fast_exp2(ml.x - m);
       l += w * ml.y;
-      acc += w * *(const float4v *)(a.part_o + prow * HD + 4 * d4);
+      acc += w * po;
     }
     acc *= 1.f / l;
   }
@@ -350,41 +604,60 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 typedef void (*SplitFn)(SplitArgs);
 
-template <int HD, int QMODE>
-SplitFn pick_split(int waves) {
-  constexpr int T = (HD == 256) ? 1 : (HD == 128 ? 2 : 4);
-  switch (waves) {
-    case 4: return split_kernel<HD, 4, T, QMODE>;
-    case 5: return split_kernel<HD, 5, T, QMODE>;
-    case 6: return split_kernel<HD, 6, T, QMODE>;
-    case 7: return split_kernel<HD, 7, T, QMODE>;
-    case 8: return split_kernel<HD, 8, T, QMODE>;
+template <int HD, int NW, int TPW, int QMODE>
+SplitFn pick_mask(int mm) {
+  switch (mm) {
+    case kMaskNone: return split_kernel<HD, NW, TPW, QMODE, kMaskNone>;
+    case kMaskDma: return split_kernel<HD, NW, TPW, QMODE, kMaskDma>;
+    case kMaskReg: return split_kernel<HD, NW, TPW, QMODE, kMaskReg>;
     default: return nullptr;
   }
 }
 
-template <int HD>
-SplitFn pick_split_q(int qmode, int waves) {
+template <int HD, int NW, int TPW>
+SplitFn pick_q(int qmode, int mm) {
   switch (qmode) {
-    case kQHiLo: return pick_split<HD, kQHiLo>(waves);
-    case kQF16: return pick_split<HD, kQF16>(waves);
-    case kQRound: return pick_split<HD, kQRound>(waves);
+    case kQHiLo: return pick_mask<HD, NW, TPW, kQHiLo>(mm);
+    case kQF16: return pick_mask<HD, NW, TPW, kQF16>(mm);
+    case kQRound: return pick_mask<HD, NW, TPW, kQRound>(mm);
     default: return nullptr;
   }
+}
+
+// Instantiated shapes: 4 waves x 1 tile, and 8 waves x 1 or (hd <= 128) 2 tiles.
+template <int HD>
+SplitFn pick_shape(int nw, int tpw, int qmode, int mm) {
+  if (nw == 4 && tpw == 1) return pick_q<HD, 4, 1>(qmode, mm);
+  if (nw == 8 && tpw == 1) return pick_q<HD, 8, 1>(qmode, mm);
+  if (HD != 256 && nw == 8 && tpw == 2) return pick_q<HD, 8, (HD == 256 ? 1 : 2)>(qmode, mm);
+  return nullptr;
 }
 
 }  // namespace
 
-int tiles_per_wave(int hd) { return hd == 256 ? 1 : (hd == 128 ? 2 : 4); }
+// Most 16-row tiles one wave of an 8-wave workgroup (256 registers per lane)
+// carries without spilling; an f32 query split into hi/lo halves doubles the
+// query registers.
+int max_tiles_per_wave(int hd, bool f16_query) {
+  if (hd == 256) return 1;
+  if (hd == 128) return f16_query ? 2 : 1;
+  return 2;
+}
 
 hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hipStream_t stream) {
+  int mm = kMaskNone;
+  if (p.mask) {
+    const bool vec = (p.n_kv % 8 == 0) && ((uintptr_t)p.mask % 16 == 0) &&
+                     (p.n_inst == 1 || p.mask_stride % 8 == 0);
+    mm = vec ? kMaskDma : kMaskReg;
+  }
   SplitFn fn = nullptr;
   switch (p.hd) {
-    case 64: fn = pick_split_q<64>(p.qmode, plan.waves); break;
-    case 128: fn = pick_split_q<128>(p.qmode, plan.waves); break;
-    case 256: fn = pick_split_q<256>(p.qmode, plan.waves); break;
+    case 64: fn = pick_shape<64>(plan.waves, plan.tiles, p.qmode, mm); break;
+    case 128: fn = pick_shape<128>(plan.waves, plan.tiles, p.qmode, mm); break;
+    case 256: fn = pick_shape<256>(plan.waves, plan.tiles, p.qmode, mm); break;
   }
-  if (!fn || plan.tiles != tiles_per_wave(p.hd)) return hipErrorInvalidValue;
+  if (!fn) return hipErrorInvalidValue;
 
   const int M = p.n_head * p.n_tok;
   SplitArgs a;
@@ -404,13 +677,17 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   a.n_split = plan.n_split;
   a.chunk = plan.chunk;
   a.n_rowblk = plan.n_rowblk;
-  a.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
+  a.scale = p.scale;
   const size_t part_o_bytes = (size_t)p.n_inst * plan.n_split * M * p.hd * sizeof(float);
   a.part_o = plan.n_split > 1 ? (float *)workspace : nullptr;
   a.part_ml = plan.n_split > 1 ? (float2v *)((char *)workspace + part_o_bytes) : nullptr;
 
+  hipEvent_t ev0, ev1;
+  profile_events(&ev0, &ev1);
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
   hipLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.waves * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
+  if (err == hipSuccess && ev1) err = hipEventRecord(ev1, stream);
   if (err != hipSuccess || plan.n_split == 1) return err;
 
   CombineArgs c;

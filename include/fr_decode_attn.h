@@ -146,7 +146,11 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device workspace bytes a call with these sizes and flags needs (0 if none),
- * or 0 with *status set when the sizes are rejected (status may be NULL). */
+ * or 0 with *status set when the sizes are rejected (status may be NULL).
+ * The launch plan depends on whether the query enters the matrix cores as one
+ * f16 operand (f16 queries, or FR_Q_ROUND_F16) or as an f32 hi/lo pair; without
+ * FR_Q_ROUND_F16 in flags the size covers both, so it also suits
+ * fr_decode_attn_q16 and FR_Q_F16 calls. */
 size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv,
                                      int hd, unsigned flags, int *status);
 
@@ -158,7 +162,8 @@ int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
 
 /*
  * The launch plan a call with these sizes would use, for tests and
- * benchmarks.  Fills up to n_info ints of info[]:
+ * benchmarks; pass FR_Q_ROUND_F16 in flags to get the plan of an f16-precision
+ * query (f16 input or rounded f32).  Fills up to n_info ints of info[]:
  *   [0] variant (1 fused, 2 decomposed)  [1] key splits per instance
  *   [2] keys per split                   [3] waves per workgroup
  *   [4] 16-row tiles per wave            [5] row blocks per instance
@@ -167,6 +172,18 @@ int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
  */
 int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd,
                         unsigned flags, int *info, int n_info);
+
+/*
+ * Optional kernel timing.  When start and stop are both non-NULL (caller-owned
+ * hipEvent_t handles passed as void*), every later call on this process
+ * records `start` on its stream immediately before its main kernel and `stop`
+ * immediately after it: the split kernel of the fused variant, or the whole
+ * three- or four-launch sequence of the decomposed one.  hipEventElapsedTime
+ * on the pair then gives that kernel's device time.  Pass NULL, NULL to stop.
+ * The setting is process-wide; calls on several host threads share it.
+ * Returns FR_OK, or FR_ERR_INVALID if exactly one event is NULL.
+ */
+int fr_decode_attn_profile_events(void *start, void *stop);
 
 /* Static, human-readable name of a status code. */
 const char *fr_status_str(int status);

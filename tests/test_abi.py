@@ -120,15 +120,33 @@ def test_plan_covers_keys_and_rows(shape, flags):
     assert p["n_split"] * p["chunk"] >= n_kv > (p["n_split"] - 1) * p["chunk"]  # no empty split
     assert p["waves"] * p["tiles"] * 16 * p["n_rowblk"] >= M
     assert p["grid"] == n_inst * p["n_rowblk"] * p["n_split"]
-    assert 4 <= p["waves"] <= 8 and p["tiles"] == {256: 1, 128: 2, 64: 4}[hd]
+    tiles_total = -(-M // 16)
+    if flags:
+        assert p["waves"] == 4 and p["tiles"] == {256: 1, 128: 2, 64: 4}[hd]
+    elif tiles_total <= 4:
+        assert p["waves"] == 4 and p["tiles"] == 1
+    else:
+        assert p["waves"] == 8 and p["tiles"] in (1, 2, 4)
+        assert p["tiles"] <= {256: 1, 128: 1, 64: 2}[hd]
     ws = B.fr_decode_attn_workspace_size(*shape, flags)
     if flags == 0:
-        rows = n_inst * p["n_split"] * M
-        want = 0 if p["n_split"] == 1 else -(-(rows * hd * 4 + rows * 8) // 256) * 256
-        assert ws == want
+        def fused_ws(pl):
+            rows = n_inst * pl["n_split"] * M
+            return 0 if pl["n_split"] == 1 else -(-(rows * hd * 4 + rows * 8) // 256) * 256
+        p16 = B.fr_decode_attn_plan(*shape, B.FR_Q_ROUND_F16)
+        assert ws == max(fused_ws(p), fused_ws(p16))
+        assert ws == B.fr_decode_attn_workspace_size(*shape, 0)
+        assert B.fr_decode_attn_workspace_size(*shape, B.FR_Q_ROUND_F16) == fused_ws(p16)
         assert p["launches"] == (1 if p["n_split"] == 1 else 2)
     else:
         assert ws >= n_inst * M * n_kv * 6 and p["launches"] >= 3
+
+
+def test_f16_queries_take_more_rows_per_workgroup_at_hd128():
+    hilo = B.fr_decode_attn_plan(1, 32, 16, 32768, 128, 0)
+    f16 = B.fr_decode_attn_plan(1, 32, 16, 32768, 128, B.FR_Q_ROUND_F16)
+    assert hilo["tiles"] == 1 and f16["tiles"] == 2
+    assert hilo["n_rowblk"] == 2 * f16["n_rowblk"]
 
 
 def test_forced_split_count(monkeypatch):
