@@ -39,6 +39,7 @@
 // rows each 16-lane group touches in a transposing read.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -567,12 +568,14 @@ struct CombineArgs {
 };
 
 // One thread per (instance, row, 4 consecutive d): merges the split partials in
-// split order.  out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, where m is
-// the largest m_s; a row with no visible key (m = -inf) is written as zeros.
-// Loops are unrolled so that each thread keeps several loads in flight.
+// split order, eight splits per round with all of a round's loads in flight
+// before any is used.  With m the running max over the splits seen (log2
+// units): out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s; a row with no
+// visible key (every m_s = -inf) is written as zeros.
 template <int HD>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int Q4 = HD / 4;
+  constexpr int R = 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.n_inst * a.M * Q4;
   if (idx >= total) return;
@@ -582,23 +585,38 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int inst = (int)(rr / a.M);
   const int64_t base = (int64_t)inst * a.n_split;
 
-  float m = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, a.part_ml[(base + s) * a.M + r].x);
+  float m = -INFINITY, l = 0.f;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  if (m != -INFINITY) {
-    float l = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < a.n_split; ++s) {
-      const int64_t prow = (base + s) * a.M + r;
-      const float2v ml = a.part_ml[prow];
-      const float4v po = *(const float4v *)(a.part_o + prow * HD + 4 * d4);
-      const float w = fast_exp2(ml.x - m);
-      l += w * ml.y;
-      acc += w * po;
+  for (int s0 = 0; s0 < a.n_split; s0 += R) {
+    float2v ml[R];
+    float4v po[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      ml[j] = float2v{-INFINITY, 0.f};
+      po[j] = float4v{0.f, 0.f, 0.f, 0.f};
+      if (s0 + j < a.n_split) {
+        const int64_t prow = (base + s0 + j) * a.M + r;
+        ml[j] = a.part_ml[prow];
+        po[j] = *(const float4v *)(a.part_o + prow * HD + 4 * d4);
+      }
     }
-    acc *= 1.f / l;
+    float mc = m;
+#pragma unroll
+    for (int j = 0; j < R; ++j) mc = fmaxf(mc, ml[j].x);
+    if (mc == -INFINITY) continue;
+    const float c = fast_exp2(m - mc);   // 0 while m = -inf
+    l *= c;
+    acc *= c;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float w = fast_exp2(ml[j].x - mc);   // 0 for a split with no visible key
+      l += w * ml[j].y;
+      acc += w * po[j];
+    }
+    m = mc;
   }
+  if (m == -INFINITY) acc = float4v{0.f, 0.f, 0.f, 0.f};
+  else acc *= 1.f / l;
   *(float4v *)(a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD + 4 * d4) = acc;
 }
 
@@ -682,12 +700,15 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   a.part_o = plan.n_split > 1 ? (float *)workspace : nullptr;
   a.part_ml = plan.n_split > 1 ? (float2v *)((char *)workspace + part_o_bytes) : nullptr;
 
+  // With profiling events installed, the launch carries them, so they take the
+  // split kernel's own start and end timestamps (no event-packet overhead).
   hipEvent_t ev0, ev1;
   profile_events(&ev0, &ev1);
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
-  hipLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.waves * 64), 0, stream, a);
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.waves * 64), 0, stream, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.waves * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
-  if (err == hipSuccess && ev1) err = hipEventRecord(ev1, stream);
   if (err != hipSuccess || plan.n_split == 1) return err;
 
   CombineArgs c;

@@ -42,6 +42,9 @@ struct Problem {
   int qmode;
 };
 
+// Integer environment override (developer knobs; fallback when unset).
+int env_int(const char *name, int fallback);
+
 // Caller events recorded around the main kernel (null when timing is off).
 void profile_events(hipEvent_t *start, hipEvent_t *stop);
 
