@@ -79,6 +79,23 @@ __device__ __forceinline__ int swz_v(int r, int gpr) {
 }
 __device__ __forceinline__ int swz_m(int t) { return t & 7; }
 
+// A copy of x the compiler cannot see through: lane-dependent address terms
+// derived from it are recomputed where they are used instead of being hoisted
+// out of the block loop and kept live (which would cost registers at the
+// loop's peak).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Keeps a computed value where it is: the empty volatile statement cannot move,
+// so the arithmetic producing x stays ahead of it instead of being sunk to its
+// first use (the softmax steps are placed between MFMA steps on purpose).
+template <typename T>
+__device__ __forceinline__ void pin(T &x) {
+  asm volatile("" : "+v"(x));
+}
+
 // 16-byte global -> LDS copy: lane l's bytes land at lds_base + 16*l.
 __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
   __builtin_amdgcn_global_load_lds((global_cvoid *)g, (lds_void *)lds_base, 16, 0, 0);
@@ -221,10 +238,11 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   uint16_t rm[2][NMR]; // register-staged mask values (kMaskReg only)
 
   // Issue every load of one 64-key block into stage `s`.
-  auto issue = [&](Stage<HD, NW> &s, int kb0, uint16_t (&rmr)[NMR]) {
+  auto issue = [&](Stage<HD, NW> &s, int kb0, uint16_t (&rmr)[NMR]) __attribute__((always_inline)) {
+    const int ln = opaque(lane);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int lin = (wave * NJ + j) * 64 + lane;   // granule index in the block
+      const int lin = (wave * NJ + j) * 64 + ln;     // granule index in the block
       const int r = lin / GPR, slot = lin % GPR;
       const int key = min(kb0 + r, a.n_kv - 1);      // rows past n_kv: any valid row
       dma16(kbase + (int64_t)key * HD + 8 * (slot ^ swz_k(r, GPR)),
@@ -233,7 +251,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
             (char *)s.v + (wave * NJ + j) * 1024);
     }
     if (MASKMODE == kMaskDma) {
-      const int lin = wave * 64 + lane;              // one granule per lane; 128 are read
+      const int lin = wave * 64 + ln;                // one granule per lane; 128 are read
       const int t = lin >> 3, gr = (lin & 7) ^ swz_m(lin >> 3);
       const bool ok = t < a.n_tok && kb0 + 8 * gr < a.n_kv;
       const uint16_t *src = ok ? mbase + (int64_t)t * a.n_kv + kb0 + 8 * gr : mbase;
@@ -250,7 +268,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   };
 
   // kMaskReg: place the register-staged values (after they have arrived).
-  auto place_mask = [&](Stage<HD, NW> &s, const uint16_t (&rmr)[NMR]) {
+  auto place_mask = [&](Stage<HD, NW> &s, const uint16_t (&rmr)[NMR]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NMR; ++i) {
       const int u = tid + i * kThreads;
@@ -265,7 +283,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   // joins every barrier); inside a wave all TPW tiles are computed, rows past
   // M carry zero queries and are never stored
   const bool wave_on = tile_base * 16 < a.M;
-  int tok[TPW];
+  const float inv_nh = 1.f / (float)a.n_head;
   // raw query values first; they are split into f16 operands only after the
   // first block has landed, so waiting on them never waits on the prefetch
   float4v qraw[TPW][KS][2];
@@ -276,7 +294,6 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   for (int i = 0; i < TPW; ++i) {
     const int tile = tile_base + kWaves * i;
     const int r = tile * 16 + l16;
-    tok[i] = min(r / a.n_head, a.n_tok - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int64_t off = (int64_t)r * HD + ks * 32 + g * 8;
@@ -350,133 +367,87 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   //   V slot of tile dt: 16*(dt/8) + ((2*(dt%8) + (q%4)/2) ^ swz_v(row)), swz_v lane-constant
   constexpr int NKO = KS < 4 ? KS : 4;
   constexpr int NVO = DT < 8 ? DT : 8;
-  int koff[NKO], voff[NVO];
-  {
-    const int krl = 8 * (l16 >> 2) + (l16 & 3);
-    const int qk = l16 & (GPR - 1);
-#pragma unroll
-    for (int j = 0; j < NKO; ++j) koff[j] = krl * HD * 2 + 16 * ((4 * j + g) ^ qk);
-    const int vrl = 8 * g + (l16 >> 2);
-    const int sv = swz_v(vrl, GPR);
-#pragma unroll
-    for (int j = 0; j < NVO; ++j)
-      voff[j] = vrl * HD * 2 + 16 * ((2 * j + ((l16 & 3) >> 1)) ^ sv) + 8 * (l16 & 1);
-  }
 
-  auto compute = [&](Stage<HD, NW> &s, int kb0) {
-    uint32_t kaddr[NKO], vaddr[NVO];
-#pragma unroll
-    for (int j = 0; j < NKO; ++j) kaddr[j] = lds_addr(s.k) + koff[j];
-#pragma unroll
-    for (int j = 0; j < NVO; ++j) vaddr[j] = lds_addr(s.v) + voff[j];
+  // ---- one 64-key block, as a software pipeline over its two 32-key halves.
+  // The MFMA work of one half runs while the softmax (VALU) of the other half
+  // is issued between its steps, so the two units overlap inside a wave:
+  //   A: S^T(h0) = K(h0).Q^T
+  //   B: S^T(h1) = K(h1).Q^T       with softmax(h0) steps in between
+  //   C: O^T += V^T(h0).P^T(h0)    with softmax(h1) steps in between
+  //   D: O^T += V^T(h1).P^T(h1)
+  // Each half updates the online-softmax state on its own; a rescale of the
+  // output (rare: the reference max only moves by more than kLazy) is applied
+  // between stages, before the PV of the half that moved it.
+  float yv[TPW][8];   // logits, then probabilities, of the half in flight
+  float bmv[TPW];     // block max of the half in flight
+  float nbv[TPW];     // -m_run * log2(e) (0 while m_run = -inf)
+  bool moved = false;
+  half8 pb[TPW][2];   // P^T of the two halves, the PV B operand
 
-    // mask values first, so their LDS latency hides behind the QK^T phase
-    half8 mh[TPW][2];
-    if (MASKMODE != kMaskNone) {
-      const uint32_t mb = lds_addr(s.m);
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const uint32_t ma0 = mb + 16 * (tok[i] * 8 + ((0 + g) ^ swz_m(tok[i])));
-        const uint32_t ma1 = mb + 16 * (tok[i] * 8 + ((4 + g) ^ swz_m(tok[i])));
-        mh[i][0] = lds_b128<0>(ma0);
-        mh[i][1] = lds_b128<0>(ma1);
-      }
-    }
-
-    // -- S^T = K . Q^T for the four 16-key tiles kt of the block.  Tile kt feeds
-    //    K rows so that lane group g ends up holding keys 32*(kt/2) + 8g +
-    //    4*(kt%2) + 0..3: per 32-key half, group g owns 8 consecutive keys.
-    //    The four K fragments of step ks+1 are read before the MFMAs of step ks.
-    float4v sc[TPW][4];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) sc[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
-    half8 kb[2][4];
-    auto kread = [&](auto KSI, half8 (&dst)[4]) {
-      constexpr int ks = decltype(KSI)::value;
-      static_for<4>([&](auto KTI) {
-        constexpr int kt = decltype(KTI)::value;
-        dst[kt] = lds_b128<256 * (ks >> 2) + (32 * (kt >> 1) + 4 * (kt & 1)) * HD * 2>(
-            kaddr[ks & 3]);
-      });
-    };
-    kread(std::integral_constant<int, 0>{}, kb[0]);
-    static_for<KS>([&](auto KSI) {
-      constexpr int ks = decltype(KSI)::value;
-      if constexpr (ks + 1 < KS) kread(std::integral_constant<int, ks + 1>{}, kb[(ks + 1) & 1]);
-      constexpr int pending = (ks + 1 < KS) ? 4 : 0;
-      wait_lgkm_tie<pending>(kb[ks & 1][0], kb[ks & 1][1], kb[ks & 1][2], kb[ks & 1][3]);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          sc[i][kt] = mfma16x16x32(kb[ks & 1][kt], qh[i][ks], sc[i][kt]);
-          if (QMODE == kQHiLo) sc[i][kt] = mfma16x16x32(kb[ks & 1][kt], ql[i][ks], sc[i][kt]);
-        }
-      }
-    });
-    // (the last wait above was lgkmcnt(0): the mask values have landed too)
-    if (MASKMODE != kMaskNone) {
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) wait_lgkm_tie<0>(mh[i][0], mh[i][1]);
-    }
-
-    // -- V^T operand reads for PV: each transposing read gives lane (q, g) the
-    //    4 keys 32hh+8g+4e+0..3 of column d = 16dt + q, the key order of P.
-    //    The first pair is issued now, ahead of the softmax arithmetic.
-    uint2v vr[2][2];
-    auto vread = [&](auto IDX, uint2v (&dst)[2]) {
-      constexpr int idx = decltype(IDX)::value;
-      constexpr int hh = idx / DT, dt = idx % DT;
-      constexpr int off = 256 * (dt >> 3) + 32 * hh * HD * 2;
-      dst[0] = lds_tr_b64<off>(vaddr[dt & 7]);
-      dst[1] = lds_tr_b64<off + 4 * HD * 2>(vaddr[dt & 7]);
-    };
-    vread(std::integral_constant<int, 0>{}, vr[0]);
-
-    // -- scale + mask (natural-log units), online softmax; pack P^T as the PV
-    //    B operand.  The reference max m_ref only moves when a block's max
-    //    exceeds it by more than kLazy (= 8 ln 2): exp(y - m_ref) then stays
-    //    at most 2^8, exact in f16, and the output rescale is almost never run.
-    const bool ragged = kb0 + KB > key_end;
-    half8 pb[TPW][2];
-    bool moved = false;
+  // Step ST (0..7) of the softmax of half HH for every tile of the wave.
+  auto sm_step = [&](auto STEP, auto HH, bool ragged, const half8 (&mh)[TPW][2],
+                     const float4v (&sc)[TPW][4], int kb0) __attribute__((always_inline)) {
+    constexpr int st = decltype(STEP)::value;
+    constexpr int hh = decltype(HH)::value;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      float y[16];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      if constexpr (st <= 1) {
+        // scale + mask in natural-log units; keys of tile kt = 2hh+st are
+        // 32hh + 8g + 4st + e for e < 4
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float m0 = MASKMODE != kMaskNone ? (float)mh[i][hh][e] : 0.f;
-          const float m1 = MASKMODE != kMaskNone ? (float)mh[i][hh][4 + e] : 0.f;
-          y[8 * hh + e] = fmaf(sc[i][2 * hh][e], a.scale, m0);
-          y[8 * hh + 4 + e] = fmaf(sc[i][2 * hh + 1][e], a.scale, m1);
+          const float m = MASKMODE != kMaskNone ? (float)mh[i][hh][4 * st + e] : 0.f;
+          yv[i][4 * st + e] = fmaf(sc[i][2 * hh + st][e], a.scale, m);
+          pin(yv[i][4 * st + e]);
         }
-      }
-      if (ragged) {
+        if (ragged) {   // uniform: only the block holding the split's end
+          const int k0 = kb0 + 32 * hh + 8 * (opaque(lane) >> 4) + 4 * st;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (kb0 + 32 * (e >> 3) + 8 * g + (e & 7) >= key_end) y[e] = -INFINITY;
-      }
-      float bm = fmaxf(fmaxf(y[0], y[1]), y[2]);
+          for (int e = 0; e < 4; ++e)
+            if (k0 + e >= key_end) yv[i][4 * st + e] = -INFINITY;
+        }
+      } else if constexpr (st == 2) {
+        float bm = fmaxf(fmaxf(yv[i][0], yv[i][1]), yv[i][2]);
+        bm = fmaxf(fmaxf(bm, yv[i][3]), yv[i][4]);
+        bmv[i] = fmaxf(fmaxf(bm, yv[i][5]), fmaxf(yv[i][6], yv[i][7]));
+        pin(bmv[i]);
+      } else if constexpr (st == 3) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmv[i]), __float_as_uint(bmv[i]),
+                                                  false, false);
+        bmv[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        pin(bmv[i]);
+      } else if constexpr (st == 4) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmv[i]), __float_as_uint(bmv[i]),
+                                                  false, false);
+        const float bm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        const float m_old = m_run[i];
+        // moves when bm exceeds the reference by more than kLazy; also taken
+        // when m_old = -inf and bm is finite (alpha = 2^-inf = 0 then)
+        const bool mv = bm > m_old + kLazy;
+        const float al = fast_exp2((m_old - bm) * kLog2e);
+        alpha[i] = mv ? al : 1.f;
+        m_run[i] = mv ? bm : m_old;
+        moved = moved || mv;
+        nbv[i] = (m_run[i] == -INFINITY) ? 0.f : -m_run[i] * kLog2e;
+        pin(nbv[i]);
+        pin(alpha[i]);
+      } else if constexpr (st <= 6) {
 #pragma unroll
-      for (int e = 3; e < 16; e += 2) bm = fmaxf(fmaxf(bm, y[e]), e + 1 < 16 ? y[e + 1] : y[e]);
-      bm = group_max(bm);
-      const float m_old = m_run[i];
-      if (bm > m_old + kLazy) {     // also taken when m_old = -inf and bm is finite
-        alpha[i] = fast_exp2((m_old - bm) * kLog2e);   // 0 when m_old = -inf
-        m_run[i] = bm;
-        moved = true;
+        for (int e = 0; e < 4; ++e) {
+          const int k = 4 * (st - 5) + e;
+          yv[i][k] = fast_exp2(fmaf(yv[i][k], kLog2e, nbv[i]));
+          pin(yv[i][k]);
+        }
       } else {
-        alpha[i] = 1.f;
-      }
-      const float nb = (m_run[i] == -INFINITY) ? 0.f : -m_run[i] * kLog2e;
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        pb[i][e >> 3][e & 7] = (_Float16)fast_exp2(fmaf(y[e], kLog2e, nb));
+        for (int e = 0; e < 8; ++e) pb[i][hh][e] = (_Float16)yv[i][e];
+        pin(pb[i][hh]);
+      }
     }
+  };
+
+  // Output rescale after a half that moved some reference max.
+  auto rescale = [&]() __attribute__((always_inline)) {
     if (__any(moved)) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
@@ -485,27 +456,162 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
         lacc[i] *= alpha[i];
       }
     }
-
-    // -- O^T += V^T . P^T over the two 32-key halves, V fragments one step ahead
-    static_for<2 * DT>([&](auto IDX) {
-      constexpr int idx = decltype(IDX)::value;
-      constexpr int hh = idx / DT, dt = idx % DT;
-      if constexpr (idx + 1 < 2 * DT) vread(std::integral_constant<int, idx + 1>{}, vr[(idx + 1) & 1]);
-      constexpr int pending = (idx + 1 < 2 * DT) ? 2 : 0;
-      wait_lgkm_tie<pending>(vr[idx & 1][0], vr[idx & 1][1]);
-      const half4 v0 = __builtin_bit_cast(half4, vr[idx & 1][0]);
-      const half4 v1 = __builtin_bit_cast(half4, vr[idx & 1][1]);
-      const half8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) o[i][dt] = mfma16x16x32(vf, pb[i][hh], o[i][dt]);
-      if constexpr (dt == 0) {
-        // row sums of the f16 probabilities on the matrix core: an all-ones
-        // A operand puts sum_k P[k][row] in every element of lacc
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) lacc[i] = mfma16x16x32(kOnes, pb[i][hh], lacc[i]);
-      }
-    });
+    moved = false;
   };
+
+  auto compute = [&](Stage<HD, NW> &s, int kb0) __attribute__((always_inline)) {
+    const bool ragged = kb0 + KB > key_end;
+    // per-lane LDS byte addresses (recomputed per block: cheaper than keeping
+    // them live).  With the swizzles above, the XOR term of a K read depends
+    // on the lane and on ks mod 4 only, and that of a V read on the lane and
+    // dt mod 8 only; everything else is a compile-time immediate.
+    //   K row of score tile kt, lane q = l16:  32*(kt/2) + 4*(kt%2) + [8*(q/4) + q%4]
+    //   K slot of step ks: (4*ks + g) ^ swz_k(row) = 16*(ks/4) + ((4*(ks%4) + g) ^ (q % GPR))
+    //   V rows of a transposing read: 32*hh + 4*e + [8*g + q/4]
+    //   V slot of tile dt: 16*(dt/8) + ((2*(dt%8) + (q%4)/2) ^ swz_v(row)), swz_v lane-constant
+    uint32_t kaddr[NKO], vaddr[NVO];
+    {
+      const int ln = opaque(lane);
+      const int l16 = ln & 15, g = ln >> 4;
+      const int krl = 8 * (l16 >> 2) + (l16 & 3);
+      const int qk = l16 & (GPR - 1);
+      const uint32_t kb = lds_addr(s.k) + krl * HD * 2;
+#pragma unroll
+      for (int j = 0; j < NKO; ++j) kaddr[j] = kb + 16 * ((4 * j + g) ^ qk);
+      const int vrl = 8 * g + (l16 >> 2);
+      const int sv = swz_v(vrl, GPR);
+      const uint32_t vb = lds_addr(s.v) + vrl * HD * 2 + 8 * (l16 & 1);
+#pragma unroll
+      for (int j = 0; j < NVO; ++j) vaddr[j] = vb + 16 * ((2 * j + ((l16 & 3) >> 1)) ^ sv);
+    }
+
+    // mask values of half HH: read ahead of the stage whose LDS waits cover
+    // them (half 0 before stage A, half 1 before stage B), so each is live
+    // only until the first softmax steps of its half
+    half8 mh[TPW][2];
+    const uint32_t mb = lds_addr(s.m);
+    auto mread = [&](auto HH) __attribute__((always_inline)) {
+      constexpr int hh = decltype(HH)::value;
+      if (MASKMODE != kMaskNone) {
+        // token of this lane's row r = tile*16 + l16: t = r / n_head, through
+        // a float reciprocal (exact here: r < 2^15 and the rounding margin is
+        // 0.5/n_head), recomputed per block rather than kept live
+        const int ln = opaque(lane);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          const int r = (tile_base + kWaves * i) * 16 + (ln & 15);
+          const int t = min((int)(((float)r + 0.5f) * inv_nh), a.n_tok - 1);
+          mh[i][hh] = lds_b128<0>(mb + 16 * (t * 8 + ((4 * hh + (ln >> 4)) ^ swz_m(t))));
+        }
+      }
+    };
+    mread(std::integral_constant<int, 0>{});
+
+    float4v sc[TPW][4];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sc[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    // S^T for half HH: K tiles kt = 2HH, 2HH+1 (keys 32HH + 8g + 4(kt%2) + 0..3
+    // in lane group g), fragments of step ks+1 read before the MFMAs of ks.
+    // after(ks) runs after the MFMAs of step ks.
+    auto qk_half = [&](auto HH, auto after) __attribute__((always_inline)) {
+      constexpr int hh = decltype(HH)::value;
+      half8 kb[2][2];
+      auto kread = [&](auto KSI, half8 (&dst)[2]) __attribute__((always_inline)) {
+        constexpr int ks = decltype(KSI)::value;
+        dst[0] = lds_b128<256 * (ks >> 2) + (32 * hh) * HD * 2>(kaddr[ks & 3]);
+        dst[1] = lds_b128<256 * (ks >> 2) + (32 * hh + 4) * HD * 2>(kaddr[ks & 3]);
+      };
+      kread(std::integral_constant<int, 0>{}, kb[0]);
+      static_for<KS>([&](auto KSI) __attribute__((always_inline)) {
+        constexpr int ks = decltype(KSI)::value;
+        if constexpr (ks + 1 < KS) kread(std::integral_constant<int, ks + 1>{}, kb[(ks + 1) & 1]);
+        wait_lgkm_tie<(ks + 1 < KS) ? 2 : 0>(kb[ks & 1][0], kb[ks & 1][1]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int i = 0; i < TPW; ++i) {
+            sc[i][2 * hh + j] = mfma16x16x32(kb[ks & 1][j], qh[i][ks], sc[i][2 * hh + j]);
+            if (QMODE == kQHiLo)
+              sc[i][2 * hh + j] = mfma16x16x32(kb[ks & 1][j], ql[i][ks], sc[i][2 * hh + j]);
+          }
+        }
+        after(KSI);
+      });
+    };
+
+    // O^T += V^T . P^T for half HH; each transposing read gives lane (q, g) the
+    // keys 32HH + 8g + 4e + 0..3 of column d = 16dt + q, the key order of P.
+    auto pv_half = [&](auto HH, auto after) __attribute__((always_inline)) {
+      constexpr int hh = decltype(HH)::value;
+      uint2v vr[2][2];
+      auto vread = [&](auto DTI, uint2v (&dst)[2]) __attribute__((always_inline)) {
+        constexpr int dt = decltype(DTI)::value;
+        constexpr int off = 256 * (dt >> 3) + 32 * hh * HD * 2;
+        dst[0] = lds_tr_b64<off>(vaddr[dt & 7]);
+        dst[1] = lds_tr_b64<off + 4 * HD * 2>(vaddr[dt & 7]);
+      };
+      vread(std::integral_constant<int, 0>{}, vr[0]);
+      static_for<DT>([&](auto DTI) __attribute__((always_inline)) {
+        constexpr int dt = decltype(DTI)::value;
+        if constexpr (dt + 1 < DT) vread(std::integral_constant<int, dt + 1>{}, vr[(dt + 1) & 1]);
+        wait_lgkm_tie<(dt + 1 < DT) ? 2 : 0>(vr[dt & 1][0], vr[dt & 1][1]);
+        const half4 v0 = __builtin_bit_cast(half4, vr[dt & 1][0]);
+        const half4 v1 = __builtin_bit_cast(half4, vr[dt & 1][1]);
+        const half8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) o[i][dt] = mfma16x16x32(vf, pb[i][hh], o[i][dt]);
+        if constexpr (dt == 0) {
+          // row sums of the f16 probabilities on the matrix core: an all-ones
+          // A operand puts sum_k P[k][row] in every element of lacc
+#pragma unroll
+          for (int i = 0; i < TPW; ++i) lacc[i] = mfma16x16x32(kOnes, pb[i][hh], lacc[i]);
+        }
+        after(DTI);
+      });
+    };
+
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    // A
+    qk_half(H0{}, [&](auto) __attribute__((always_inline)) {});
+    // (the last wait of stage A was lgkmcnt(0): the half-0 mask has landed)
+    if (MASKMODE != kMaskNone) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) wait_lgkm_tie<0>(mh[i][0]);
+    }
+    mread(std::integral_constant<int, 1>{});
+    // B: softmax steps [8ks/KS, 8(ks+1)/KS) of half 0 after QK step ks of half 1
+    qk_half(H1{}, [&](auto KSI) __attribute__((always_inline)) {
+      constexpr int ks = decltype(KSI)::value;
+      static_for<8>([&](auto STI) __attribute__((always_inline)) {
+        constexpr int stp = decltype(STI)::value;
+        if constexpr (stp * KS >= 8 * ks && stp * KS < 8 * (ks + 1))
+          sm_step(STI, H0{}, ragged, mh, sc, kb0);
+      });
+    });
+    // (the last wait of stage B was lgkmcnt(0): the half-1 mask has landed)
+    if (MASKMODE != kMaskNone) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) wait_lgkm_tie<0>(mh[i][1]);
+    }
+    rescale();
+    // C: softmax steps of half 1 after PV step dt of half 0
+    pv_half(H0{}, [&](auto DTI) __attribute__((always_inline)) {
+      constexpr int dt = decltype(DTI)::value;
+      static_for<8>([&](auto STI) __attribute__((always_inline)) {
+        constexpr int stp = decltype(STI)::value;
+        if constexpr (stp * DT >= 8 * dt && stp * DT < 8 * (dt + 1))
+          sm_step(STI, H1{}, ragged, mh, sc, kb0);
+      });
+    });
+    rescale();
+    // D
+    pv_half(H1{}, [&](auto) __attribute__((always_inline)) {});
+  };
+
 
   // ---- main loop: two blocks per trip, st0 then st1.  Invariant at the top
   // of a trip: block b is complete in st0 and only block b+1 (into st1) may
@@ -567,46 +673,50 @@ struct CombineArgs {
   int M, n_split, n_inst;
 };
 
-// One thread per (instance, row, 4 consecutive d): merges the split partials in
-// split order, eight splits per round with all of a round's loads in flight
-// before any is used.  With m the running max over the splits seen (log2
-// units): out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s; a row with no
-// visible key (every m_s = -inf) is written as zeros.
+// One workgroup per (instance, row): 256 threads = G split groups x (HD/4)
+// columns of 4 consecutive d.  Thread (g, c) merges splits g, g+G, g+2G, ...
+// (all of its loads in flight together), then the G group results are merged
+// in group order through LDS.  With m the running max (log2 units):
+//   out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s
+// A split with no visible key has m_s = -inf and weight 0; a row with no
+// visible key at all is written as zeros.  The merge order is fixed, so the
+// result does not depend on timing.
 template <int HD>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  constexpr int Q4 = HD / 4;
-  constexpr int R = 8;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.n_inst * a.M * Q4;
-  if (idx >= total) return;
-  const int d4 = (int)(idx % Q4);
-  const int64_t rr = idx / Q4;
-  const int r = (int)(rr % a.M);
-  const int inst = (int)(rr / a.M);
+  constexpr int C = HD / 4;          // float4 columns per row
+  constexpr int G = 256 / C;         // split groups
+  constexpr int R = 8;               // loads in flight per thread per round
+  __shared__ float4v s_acc[G][C];
+  __shared__ float s_m[G][C], s_l[G][C];
+
+  const int c = threadIdx.x % C, g = threadIdx.x / C;
+  const int r = blockIdx.x % a.M;
+  const int inst = blockIdx.x / a.M;
   const int64_t base = (int64_t)inst * a.n_split;
 
   float m = -INFINITY, l = 0.f;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < a.n_split; s0 += R) {
+  for (int s0 = g; s0 < a.n_split; s0 += G * R) {
     float2v ml[R];
     float4v po[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       ml[j] = float2v{-INFINITY, 0.f};
       po[j] = float4v{0.f, 0.f, 0.f, 0.f};
-      if (s0 + j < a.n_split) {
-        const int64_t prow = (base + s0 + j) * a.M + r;
+      const int sp = s0 + j * G;
+      if (sp < a.n_split) {
+        const int64_t prow = (base + sp) * a.M + r;
         ml[j] = a.part_ml[prow];
-        po[j] = *(const float4v *)(a.part_o + prow * HD + 4 * d4);
+        po[j] = *(const float4v *)(a.part_o + prow * HD + 4 * c);
       }
     }
     float mc = m;
 #pragma unroll
     for (int j = 0; j < R; ++j) mc = fmaxf(mc, ml[j].x);
     if (mc == -INFINITY) continue;
-    const float c = fast_exp2(m - mc);   // 0 while m = -inf
-    l *= c;
-    acc *= c;
+    const float k = fast_exp2(m - mc);   // 0 while m = -inf
+    l *= k;
+    acc *= k;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const float w = fast_exp2(ml[j].x - mc);   // 0 for a split with no visible key
@@ -615,9 +725,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
     m = mc;
   }
-  if (m == -INFINITY) acc = float4v{0.f, 0.f, 0.f, 0.f};
-  else acc *= 1.f / l;
-  *(float4v *)(a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD + 4 * d4) = acc;
+  s_acc[g][c] = acc;
+  s_m[g][c] = m;
+  s_l[g][c] = l;
+  __syncthreads();
+  if (g != 0) return;
+  float mm = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < G; ++j) mm = fmaxf(mm, s_m[j][c]);
+  float4v out = {0.f, 0.f, 0.f, 0.f};
+  if (mm != -INFINITY) {
+    float ll = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float w = fast_exp2(s_m[j][c] - mm);
+      ll += w * s_l[j][c];
+      out += w * s_acc[j][c];
+    }
+    out *= 1.f / ll;
+  }
+  *(float4v *)(a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD + 4 * c) = out;
 }
 
 typedef void (*SplitFn)(SplitArgs);
@@ -642,12 +769,19 @@ SplitFn pick_q(int qmode, int mm) {
   }
 }
 
-// Instantiated shapes: 4 waves x 1 tile, and 8 waves x 1 or (hd <= 128) 2 tiles.
+// Instantiated shapes: 4 waves x 1 tile, 8 waves x 1 tile, and 8 waves x 2
+// tiles for hd 64 (any query mode) and hd 128 (single f16 query operand only:
+// the hi/lo pair does not fit the register budget there).
 template <int HD>
 SplitFn pick_shape(int nw, int tpw, int qmode, int mm) {
   if (nw == 4 && tpw == 1) return pick_q<HD, 4, 1>(qmode, mm);
   if (nw == 8 && tpw == 1) return pick_q<HD, 8, 1>(qmode, mm);
-  if (HD != 256 && nw == 8 && tpw == 2) return pick_q<HD, 8, (HD == 256 ? 1 : 2)>(qmode, mm);
+  if constexpr (HD == 64) {
+    if (nw == 8 && tpw == 2) return pick_q<HD, 8, 2>(qmode, mm);
+  } else if constexpr (HD == 128) {
+    if (nw == 8 && tpw == 2 && qmode == kQF16) return pick_mask<HD, 8, 2, kQF16>(mm);
+    if (nw == 8 && tpw == 2 && qmode == kQRound) return pick_mask<HD, 8, 2, kQRound>(mm);
+  }
   return nullptr;
 }
 
@@ -719,8 +853,7 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   c.M = M;
   c.n_split = plan.n_split;
   c.n_inst = p.n_inst;
-  const int64_t threads = (int64_t)p.n_inst * M * (p.hd / 4);
-  const int blocks = (int)((threads + 255) / 256);
+  const int blocks = p.n_inst * M;   // one workgroup per output row
   switch (p.hd) {
     case 64: hipLaunchKernelGGL(combine_kernel<64>, dim3(blocks), dim3(256), 0, stream, c); break;
     case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(blocks), dim3(256), 0, stream, c); break;
