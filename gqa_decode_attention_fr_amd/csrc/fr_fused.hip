@@ -79,15 +79,6 @@ __device__ __forceinline__ int swz_v(int r, int gpr) {
 }
 __device__ __forceinline__ int swz_m(int t) { return t & 7; }
 
-// A copy of x the compiler cannot see through: lane-dependent address terms
-// derived from it are recomputed where they are used instead of being hoisted
-// out of the block loop and kept live (which would cost registers at the
-// loop's peak).
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 // Keeps a computed value where it is: the empty volatile statement cannot move,
 // so the arithmetic producing x stays ahead of it instead of being sunk to its
 // first use (the softmax steps are placed between MFMA steps on purpose).
@@ -237,24 +228,48 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 
   uint16_t rm[2][NMR]; // register-staged mask values (kMaskReg only)
 
-  // Issue every load of one 64-key block into stage `s`.
+  // Per-lane DMA source offsets (elements), fixed for the whole kernel.
+  // Granule lin = (wave*NJ + j)*64 + lane of a block is K/V row
+  // r = lin / GPR, 16-byte slot lin % GPR = lane % GPR; it lands at LDS slot
+  // slot ^ swz(r).  Only the block's first key moves between blocks.
+  constexpr int RPI = 64 / GPR;                       // rows per DMA instruction
+  int dma_kofs[NJ], dma_vofs[NJ], dma_row[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int r = (wave * NJ + j) * RPI + lane / GPR;
+    const int slot = lane % GPR;
+    dma_row[j] = r;
+    dma_kofs[j] = r * HD + 8 * (slot ^ swz_k(r, GPR));
+    dma_vofs[j] = r * HD + 8 * (slot ^ swz_v(r, GPR));
+  }
+  // mask granule of this lane: token t = lin / 8, key group (lin % 8) ^ swz_m(t)
+  const int m_lin = wave * 64 + lane;
+  const int m_tok = m_lin >> 3;
+  const int m_gr = (m_lin & 7) ^ swz_m(m_lin >> 3);
+  const int m_ofs = m_tok < a.n_tok ? m_tok * a.n_kv + 8 * m_gr : 0;   // < 2^31
+
+  // Issue every load of one 64-key block into stage `s`.  Blocks that reach
+  // past n_kv (at most the last) clamp their rows to a valid one and read the
+  // mask granules past n_kv from a valid address (those keys are dropped by
+  // the ragged-block handling of the softmax).
   auto issue = [&](Stage<HD, NW> &s, int kb0, uint16_t (&rmr)[NMR]) __attribute__((always_inline)) {
-    const int ln = opaque(lane);
+    const bool full = kb0 + KB <= a.n_kv;
+    const uint16_t *kb = kbase + (int64_t)kb0 * HD;
+    const uint16_t *vb = vbase + (int64_t)kb0 * HD;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int lin = (wave * NJ + j) * 64 + ln;     // granule index in the block
-      const int r = lin / GPR, slot = lin % GPR;
-      const int key = min(kb0 + r, a.n_kv - 1);      // rows past n_kv: any valid row
-      dma16(kbase + (int64_t)key * HD + 8 * (slot ^ swz_k(r, GPR)),
-            (char *)s.k + (wave * NJ + j) * 1024);
-      dma16(vbase + (int64_t)key * HD + 8 * (slot ^ swz_v(r, GPR)),
-            (char *)s.v + (wave * NJ + j) * 1024);
+      int ko = dma_kofs[j], vo = dma_vofs[j];
+      if (!full) {
+        const int back = max(kb0 + dma_row[j] - (a.n_kv - 1), 0) * HD;   // rows past n_kv
+        ko -= back;
+        vo -= back;
+      }
+      dma16(kb + ko, (char *)s.k + (wave * NJ + j) * 1024);
+      dma16(vb + vo, (char *)s.v + (wave * NJ + j) * 1024);
     }
     if (MASKMODE == kMaskDma) {
-      const int lin = wave * 64 + ln;                // one granule per lane; 128 are read
-      const int t = lin >> 3, gr = (lin & 7) ^ swz_m(lin >> 3);
-      const bool ok = t < a.n_tok && kb0 + 8 * gr < a.n_kv;
-      const uint16_t *src = ok ? mbase + (int64_t)t * a.n_kv + kb0 + 8 * gr : mbase;
+      const bool ok = m_tok < a.n_tok && (full || kb0 + 8 * m_gr < a.n_kv);
+      const uint16_t *src = ok ? mbase + (int64_t)kb0 + m_ofs : mbase;
       dma16(src, (char *)s.m + wave * 1024);
     } else if (MASKMODE == kMaskReg) {
 #pragma unroll
@@ -283,7 +298,6 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   // joins every barrier); inside a wave all TPW tiles are computed, rows past
   // M carry zero queries and are never stored
   const bool wave_on = tile_base * 16 < a.M;
-  const float inv_nh = 1.f / (float)a.n_head;
   // raw query values first; they are split into f16 operands only after the
   // first block has landed, so waiting on them never waits on the prefetch
   float4v qraw[TPW][KS][2];
@@ -368,6 +382,44 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   constexpr int NKO = KS < 4 ? KS : 4;
   constexpr int NVO = DT < 8 ? DT : 8;
 
+  // ---- per-lane LDS byte addresses of the compute phase, for both stages.
+  // With the swizzles above, the XOR term of a K read depends on the lane and
+  // on ks mod 4 only, and that of a V read on the lane and dt mod 8 only;
+  // everything else is a compile-time immediate.
+  //   K row of score tile kt, lane q = l16:  32*(kt/2) + 4*(kt%2) + [8*(q/4) + q%4]
+  //   K slot of step ks: (4*ks + g) ^ swz_k(row) = 16*(ks/4) + ((4*(ks%4) + g) ^ (q % GPR))
+  //   V rows of a transposing read: 32*hh + 4*e + [8*g + q/4]
+  //   V slot of tile dt: 16*(dt/8) + ((2*(dt%8) + (q%4)/2) ^ swz_v(row)), swz_v lane-constant
+  //   mask granule of token t, half hh: t*8 + ((4*hh + g) ^ swz_m(t))
+  uint32_t kaddr_s[2][NKO], vaddr_s[2][NVO], maddr_s[2][TPW][2];
+  {
+    const int krl = 8 * (l16 >> 2) + (l16 & 3);
+    const int qk = l16 & (GPR - 1);
+    const int vrl = 8 * g + (l16 >> 2);
+    const int sv = swz_v(vrl, GPR);
+    const float inv_nh = 1.f / (float)a.n_head;
+#pragma unroll
+    for (int si = 0; si < 2; ++si) {
+      Stage<HD, NW> &st = si ? st1 : st0;
+      const uint32_t kb = lds_addr(st.k) + krl * HD * 2;
+#pragma unroll
+      for (int j = 0; j < NKO; ++j) kaddr_s[si][j] = kb + 16 * ((4 * j + g) ^ qk);
+      const uint32_t vb = lds_addr(st.v) + vrl * HD * 2 + 8 * (l16 & 1);
+#pragma unroll
+      for (int j = 0; j < NVO; ++j) vaddr_s[si][j] = vb + 16 * ((2 * j + ((l16 & 3) >> 1)) ^ sv);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        // token of this lane's row r = tile*16 + l16: t = r / n_head through a
+        // float reciprocal (exact: r < 2^15 and the rounding margin is 0.5/n_head)
+        const int r = (tile_base + kWaves * i) * 16 + l16;
+        const int t = min((int)(((float)r + 0.5f) * inv_nh), a.n_tok - 1);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          maddr_s[si][i][hh] = lds_addr(st.m) + 16 * (t * 8 + ((4 * hh + g) ^ swz_m(t)));
+      }
+    }
+  }
+
   // ---- one 64-key block, as a software pipeline over its two 32-key halves.
   // The MFMA work of one half runs while the softmax (VALU) of the other half
   // is issued between its steps, so the two units overlap inside a wave:
@@ -386,7 +438,9 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 
   // Step ST (0..7) of the softmax of half HH for every tile of the wave.
   auto sm_step = [&](auto STEP, auto HH, bool ragged, const half8 (&mh)[TPW][2],
-                     const float4v (&sc)[TPW][4], int kb0) __attribute__((always_inline)) {
+                     const float4v (&sc)[TPW][4], const auto &sc2, int kb0)
+                     __attribute__((always_inline)) {
+    constexpr bool split_acc = sizeof(sc2[0]) == sizeof(sc[0]);   // 4 kt entries
     constexpr int st = decltype(STEP)::value;
     constexpr int hh = decltype(HH)::value;
 #pragma unroll
@@ -397,11 +451,13 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float m = MASKMODE != kMaskNone ? (float)mh[i][hh][4 * st + e] : 0.f;
-          yv[i][4 * st + e] = fmaf(sc[i][2 * hh + st][e], a.scale, m);
+          float sv = sc[i][2 * hh + st][e];
+          if constexpr (split_acc) sv += sc2[i][2 * hh + st][e];
+          yv[i][4 * st + e] = fmaf(sv, a.scale, m);
           pin(yv[i][4 * st + e]);
         }
         if (ragged) {   // uniform: only the block holding the split's end
-          const int k0 = kb0 + 32 * hh + 8 * (opaque(lane) >> 4) + 4 * st;
+          const int k0 = kb0 + 32 * hh + 8 * g + 4 * st;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (k0 + e >= key_end) yv[i][4 * st + e] = -INFINITY;
@@ -459,83 +515,78 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     moved = false;
   };
 
-  auto compute = [&](Stage<HD, NW> &s, int kb0) __attribute__((always_inline)) {
+  auto compute = [&](auto SI, int kb0) __attribute__((always_inline)) {
+    constexpr int si = decltype(SI)::value;
     const bool ragged = kb0 + KB > key_end;
-    // per-lane LDS byte addresses (recomputed per block: cheaper than keeping
-    // them live).  With the swizzles above, the XOR term of a K read depends
-    // on the lane and on ks mod 4 only, and that of a V read on the lane and
-    // dt mod 8 only; everything else is a compile-time immediate.
-    //   K row of score tile kt, lane q = l16:  32*(kt/2) + 4*(kt%2) + [8*(q/4) + q%4]
-    //   K slot of step ks: (4*ks + g) ^ swz_k(row) = 16*(ks/4) + ((4*(ks%4) + g) ^ (q % GPR))
-    //   V rows of a transposing read: 32*hh + 4*e + [8*g + q/4]
-    //   V slot of tile dt: 16*(dt/8) + ((2*(dt%8) + (q%4)/2) ^ swz_v(row)), swz_v lane-constant
-    uint32_t kaddr[NKO], vaddr[NVO];
-    {
-      const int ln = opaque(lane);
-      const int l16 = ln & 15, g = ln >> 4;
-      const int krl = 8 * (l16 >> 2) + (l16 & 3);
-      const int qk = l16 & (GPR - 1);
-      const uint32_t kb = lds_addr(s.k) + krl * HD * 2;
-#pragma unroll
-      for (int j = 0; j < NKO; ++j) kaddr[j] = kb + 16 * ((4 * j + g) ^ qk);
-      const int vrl = 8 * g + (l16 >> 2);
-      const int sv = swz_v(vrl, GPR);
-      const uint32_t vb = lds_addr(s.v) + vrl * HD * 2 + 8 * (l16 & 1);
-#pragma unroll
-      for (int j = 0; j < NVO; ++j) vaddr[j] = vb + 16 * ((2 * j + ((l16 & 3) >> 1)) ^ sv);
-    }
+    const uint32_t(&kaddr)[NKO] = kaddr_s[si];
+    const uint32_t(&vaddr)[NVO] = vaddr_s[si];
 
     // mask values of half HH: read ahead of the stage whose LDS waits cover
     // them (half 0 before stage A, half 1 before stage B), so each is live
     // only until the first softmax steps of its half
     half8 mh[TPW][2];
-    const uint32_t mb = lds_addr(s.m);
     auto mread = [&](auto HH) __attribute__((always_inline)) {
       constexpr int hh = decltype(HH)::value;
       if (MASKMODE != kMaskNone) {
-        // token of this lane's row r = tile*16 + l16: t = r / n_head, through
-        // a float reciprocal (exact here: r < 2^15 and the rounding margin is
-        // 0.5/n_head), recomputed per block rather than kept live
-        const int ln = opaque(lane);
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          const int r = (tile_base + kWaves * i) * 16 + (ln & 15);
-          const int t = min((int)(((float)r + 0.5f) * inv_nh), a.n_tok - 1);
-          mh[i][hh] = lds_b128<0>(mb + 16 * (t * 8 + ((4 * hh + (ln >> 4)) ^ swz_m(t))));
-        }
+        for (int i = 0; i < TPW; ++i) mh[i][hh] = lds_b128<0>(maddr_s[si][i][hh]);
       }
     };
     mread(std::integral_constant<int, 0>{});
 
-    float4v sc[TPW][4];
+    // Score accumulators.  With one tile per wave the two K tiles of a half
+    // would give only two dependent MFMA chains; a second accumulator set
+    // (the lo query half, or odd ks for a single f16 operand) doubles that,
+    // and is added in when the scores are read.
+    constexpr bool kSplitAcc = TPW == 1 && HD <= 128;
+    constexpr int NSA = kSplitAcc ? 4 : 1;
+    float4v sc[TPW][4], sc2[TPW][NSA];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
+    for (int i = 0; i < TPW; ++i) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) sc[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < NSA; ++kt) sc2[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // LDS prefetch distance (steps ahead) of the K and V fragment reads:
+    // deeper where the register budget allows.
+    constexpr int PD = HD <= 128 ? 2 : 1;
 
     // S^T for half HH: K tiles kt = 2HH, 2HH+1 (keys 32HH + 8g + 4(kt%2) + 0..3
-    // in lane group g), fragments of step ks+1 read before the MFMAs of ks.
+    // in lane group g), fragments read PD steps ahead of their MFMAs.
     // after(ks) runs after the MFMAs of step ks.
     auto qk_half = [&](auto HH, auto after) __attribute__((always_inline)) {
       constexpr int hh = decltype(HH)::value;
-      half8 kb[2][2];
-      auto kread = [&](auto KSI, half8 (&dst)[2]) __attribute__((always_inline)) {
+      half8 kb[PD + 1][2];
+      auto kread = [&](auto KSI) __attribute__((always_inline)) {
         constexpr int ks = decltype(KSI)::value;
-        dst[0] = lds_b128<256 * (ks >> 2) + (32 * hh) * HD * 2>(kaddr[ks & 3]);
-        dst[1] = lds_b128<256 * (ks >> 2) + (32 * hh + 4) * HD * 2>(kaddr[ks & 3]);
+        kb[ks % (PD + 1)][0] = lds_b128<256 * (ks >> 2) + (32 * hh) * HD * 2>(kaddr[ks & 3]);
+        kb[ks % (PD + 1)][1] = lds_b128<256 * (ks >> 2) + (32 * hh + 4) * HD * 2>(kaddr[ks & 3]);
       };
-      kread(std::integral_constant<int, 0>{}, kb[0]);
+      static_for<(PD < KS ? PD : KS)>([&](auto KSI) __attribute__((always_inline)) { kread(KSI); });
       static_for<KS>([&](auto KSI) __attribute__((always_inline)) {
         constexpr int ks = decltype(KSI)::value;
-        if constexpr (ks + 1 < KS) kread(std::integral_constant<int, ks + 1>{}, kb[(ks + 1) & 1]);
-        wait_lgkm_tie<(ks + 1 < KS) ? 2 : 0>(kb[ks & 1][0], kb[ks & 1][1]);
+        if constexpr (ks + PD < KS) kread(std::integral_constant<int, ks + PD>{});
+        // reads issued after those of step ks: 2 per later step in flight
+        constexpr int later = (KS - 1 - ks < PD ? KS - 1 - ks : PD);
+        wait_lgkm_tie<2 * later>(kb[ks % (PD + 1)][0], kb[ks % (PD + 1)][1]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
           for (int i = 0; i < TPW; ++i) {
-            sc[i][2 * hh + j] = mfma16x16x32(kb[ks & 1][j], qh[i][ks], sc[i][2 * hh + j]);
-            if (QMODE == kQHiLo)
-              sc[i][2 * hh + j] = mfma16x16x32(kb[ks & 1][j], ql[i][ks], sc[i][2 * hh + j]);
+            const half8 kf = kb[ks % (PD + 1)][j];
+            if constexpr (kSplitAcc && QMODE == kQHiLo) {
+              sc[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc[i][2 * hh + j]);
+              sc2[i][2 * hh + j] = mfma16x16x32(kf, ql[i][ks], sc2[i][2 * hh + j]);
+            } else if constexpr (kSplitAcc) {
+              if constexpr (ks & 1) sc2[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc2[i][2 * hh + j]);
+              else sc[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc[i][2 * hh + j]);
+            } else {
+              sc[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc[i][2 * hh + j]);
+              if (QMODE == kQHiLo)
+                sc[i][2 * hh + j] = mfma16x16x32(kf, ql[i][ks], sc[i][2 * hh + j]);
+            }
           }
         }
         after(KSI);
@@ -546,20 +597,21 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     // keys 32HH + 8g + 4e + 0..3 of column d = 16dt + q, the key order of P.
     auto pv_half = [&](auto HH, auto after) __attribute__((always_inline)) {
       constexpr int hh = decltype(HH)::value;
-      uint2v vr[2][2];
-      auto vread = [&](auto DTI, uint2v (&dst)[2]) __attribute__((always_inline)) {
+      uint2v vr[PD + 1][2];
+      auto vread = [&](auto DTI) __attribute__((always_inline)) {
         constexpr int dt = decltype(DTI)::value;
         constexpr int off = 256 * (dt >> 3) + 32 * hh * HD * 2;
-        dst[0] = lds_tr_b64<off>(vaddr[dt & 7]);
-        dst[1] = lds_tr_b64<off + 4 * HD * 2>(vaddr[dt & 7]);
+        vr[dt % (PD + 1)][0] = lds_tr_b64<off>(vaddr[dt & 7]);
+        vr[dt % (PD + 1)][1] = lds_tr_b64<off + 4 * HD * 2>(vaddr[dt & 7]);
       };
-      vread(std::integral_constant<int, 0>{}, vr[0]);
+      static_for<(PD < DT ? PD : DT)>([&](auto DTI) __attribute__((always_inline)) { vread(DTI); });
       static_for<DT>([&](auto DTI) __attribute__((always_inline)) {
         constexpr int dt = decltype(DTI)::value;
-        if constexpr (dt + 1 < DT) vread(std::integral_constant<int, dt + 1>{}, vr[(dt + 1) & 1]);
-        wait_lgkm_tie<(dt + 1 < DT) ? 2 : 0>(vr[dt & 1][0], vr[dt & 1][1]);
-        const half4 v0 = __builtin_bit_cast(half4, vr[dt & 1][0]);
-        const half4 v1 = __builtin_bit_cast(half4, vr[dt & 1][1]);
+        if constexpr (dt + PD < DT) vread(std::integral_constant<int, dt + PD>{});
+        constexpr int later = (DT - 1 - dt < PD ? DT - 1 - dt : PD);
+        wait_lgkm_tie<2 * later>(vr[dt % (PD + 1)][0], vr[dt % (PD + 1)][1]);
+        const half4 v0 = __builtin_bit_cast(half4, vr[dt % (PD + 1)][0]);
+        const half4 v1 = __builtin_bit_cast(half4, vr[dt % (PD + 1)][1]);
         const half8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
         for (int i = 0; i < TPW; ++i) o[i][dt] = mfma16x16x32(vf, pb[i][hh], o[i][dt]);
@@ -589,7 +641,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       static_for<8>([&](auto STI) __attribute__((always_inline)) {
         constexpr int stp = decltype(STI)::value;
         if constexpr (stp * KS >= 8 * ks && stp * KS < 8 * (ks + 1))
-          sm_step(STI, H0{}, ragged, mh, sc, kb0);
+          sm_step(STI, H0{}, ragged, mh, sc, sc2, kb0);
       });
     });
     // (the last wait of stage B was lgkmcnt(0): the half-1 mask has landed)
@@ -604,7 +656,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       static_for<8>([&](auto STI) __attribute__((always_inline)) {
         constexpr int stp = decltype(STI)::value;
         if constexpr (stp * DT >= 8 * dt && stp * DT < 8 * (dt + 1))
-          sm_step(STI, H1{}, ragged, mh, sc, kb0);
+          sm_step(STI, H1{}, ragged, mh, sc, sc2, kb0);
       });
     });
     rescale();
@@ -623,7 +675,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       wait_lgkm<0>();
     }
     barrier();
-    if (wave_on) compute(st0, key_begin + b * KB);
+    if (wave_on) compute(std::integral_constant<int, 0>{}, key_begin + b * KB);
     barrier();
     if (b + 2 < nblk) issue(st0, key_begin + (b + 2) * KB, rm[0]);
     if (b + 1 >= nblk) break;
@@ -633,7 +685,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       wait_lgkm<0>();
     }
     barrier();
-    if (wave_on) compute(st1, key_begin + (b + 1) * KB);
+    if (wave_on) compute(std::integral_constant<int, 1>{}, key_begin + (b + 1) * KB);
     barrier();
     if (b + 3 < nblk) {
       issue(st1, key_begin + (b + 3) * KB, rm[1]);
