@@ -711,7 +711,9 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       const int64_t prow = ((int64_t)inst * a.n_split + split) * a.M + r;
       float *po = a.part_o + prow * HD;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *(float4v *)(po + dt * 16 + 4 * g) = o[i][dt];
+      // streaming stores: the partials are read once, by the combine kernel
+      for (int dt = 0; dt < DT; ++dt)
+        __builtin_nontemporal_store(o[i][dt], (float4v *)(po + dt * 16 + 4 * g));
       if (g == 0) a.part_ml[prow] = float2v{m_run[i] * kLog2e, l};  // max in log2 units
     }
   }
