@@ -326,13 +326,13 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   }
   asm volatile("" ::: "memory"); // query loads are issued before the block loads
 
+  // The queries and block 0 first, alone: every workgroup starts at once, so
+  // requesting block 1 as well would make block 0 (and the start of the
+  // arithmetic) wait behind the whole machine's block-1 traffic.  Block 1 is
+  // issued once block 0 has landed and loads while block 0 is computed.
   issue(st0, key_begin, rm[0]);
-  if (nblk > 1) {
-    issue(st1, key_begin + KB, rm[1]);
-    wait_vm<J>();
-  } else {
-    wait_vm<0>();
-  }
+  wait_vm<0>();
+  if (nblk > 1) issue(st1, key_begin + KB, rm[1]);
 
   half8 qh[TPW][KS], ql[TPW][KS];
 #pragma unroll
