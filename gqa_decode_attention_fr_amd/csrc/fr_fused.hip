@@ -204,8 +204,15 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   constexpr int KS = HD / 32;
   constexpr int DT = HD / 16;
 
-  __shared__ __attribute__((aligned(16))) Stage<HD, NW> st0;
-  __shared__ __attribute__((aligned(16))) Stage<HD, NW> st1;
+  __shared__ __attribute__((aligned(16))) Stage<HD, NW> stg[2];
+  Stage<HD, NW> &st0 = stg[0];
+  Stage<HD, NW> &st1 = stg[1];
+  // Stage 1 sits a fixed distance after stage 0; where that distance fits the
+  // 16-bit immediate offset of an LDS read (hd <= 128), stage-1 reads reuse
+  // the stage-0 lane addresses with a larger immediate.
+  constexpr int kStageBytes = (int)sizeof(Stage<HD, NW>);
+  constexpr bool kImmStage = HD <= 128;
+  constexpr int NAS = kImmStage ? 1 : 2;   // lane address sets kept
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   //   V rows of a transposing read: 32*hh + 4*e + [8*g + q/4]
   //   V slot of tile dt: 16*(dt/8) + ((2*(dt%8) + (q%4)/2) ^ swz_v(row)), swz_v lane-constant
   //   mask granule of token t, half hh: t*8 + ((4*hh + g) ^ swz_m(t))
-  uint32_t kaddr_s[2][NKO], vaddr_s[2][NVO], maddr_s[2][TPW][2];
+  uint32_t kaddr_s[NAS][NKO], vaddr_s[NAS][NVO], maddr_s[NAS][TPW][2];
   {
     const int krl = 8 * (l16 >> 2) + (l16 & 3);
     const int qk = l16 & (GPR - 1);
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     const int sv = swz_v(vrl, GPR);
     const float inv_nh = 1.f / (float)a.n_head;
 #pragma unroll
-    for (int si = 0; si < 2; ++si) {
+    for (int si = 0; si < NAS; ++si) {
       Stage<HD, NW> &st = si ? st1 : st0;
       const uint32_t kb = lds_addr(st.k) + krl * HD * 2;
 #pragma unroll
@@ -518,8 +525,10 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   auto compute = [&](auto SI, int kb0) __attribute__((always_inline)) {
     constexpr int si = decltype(SI)::value;
     const bool ragged = kb0 + KB > key_end;
-    const uint32_t(&kaddr)[NKO] = kaddr_s[si];
-    const uint32_t(&vaddr)[NVO] = vaddr_s[si];
+    constexpr int asi = kImmStage ? 0 : si;              // lane address set
+    constexpr int SOFF = kImmStage ? si * kStageBytes : 0; // extra immediate offset
+    const uint32_t(&kaddr)[NKO] = kaddr_s[asi];
+    const uint32_t(&vaddr)[NVO] = vaddr_s[asi];
 
     // mask values of half HH: read ahead of the stage whose LDS waits cover
     // them (half 0 before stage A, half 1 before stage B), so each is live
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       constexpr int hh = decltype(HH)::value;
       if (MASKMODE != kMaskNone) {
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) mh[i][hh] = lds_b128<0>(maddr_s[si][i][hh]);
+        for (int i = 0; i < TPW; ++i) mh[i][hh] = lds_b128<SOFF>(maddr_s[asi][i][hh]);
       }
     };
     mread(std::integral_constant<int, 0>{});
@@ -550,8 +559,8 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     }
 
     // LDS prefetch distance (steps ahead) of the K and V fragment reads:
-    // deeper where the register budget allows.
-    constexpr int PD = HD <= 128 ? 2 : 1;
+    // deeper where the register budget allows (one tile per wave, hd <= 128).
+    constexpr int PD = (HD <= 128 && TPW == 1) ? 2 : 1;
 
     // S^T for half HH: K tiles kt = 2HH, 2HH+1 (keys 32HH + 8g + 4(kt%2) + 0..3
     // in lane group g), fragments read PD steps ahead of their MFMAs.
@@ -561,8 +570,9 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       half8 kb[PD + 1][2];
       auto kread = [&](auto KSI) __attribute__((always_inline)) {
         constexpr int ks = decltype(KSI)::value;
-        kb[ks % (PD + 1)][0] = lds_b128<256 * (ks >> 2) + (32 * hh) * HD * 2>(kaddr[ks & 3]);
-        kb[ks % (PD + 1)][1] = lds_b128<256 * (ks >> 2) + (32 * hh + 4) * HD * 2>(kaddr[ks & 3]);
+        kb[ks % (PD + 1)][0] = lds_b128<SOFF + 256 * (ks >> 2) + (32 * hh) * HD * 2>(kaddr[ks & 3]);
+        kb[ks % (PD + 1)][1] =
+            lds_b128<SOFF + 256 * (ks >> 2) + (32 * hh + 4) * HD * 2>(kaddr[ks & 3]);
       };
       static_for<(PD < KS ? PD : KS)>([&](auto KSI) __attribute__((always_inline)) { kread(KSI); });
       static_for<KS>([&](auto KSI) __attribute__((always_inline)) {
@@ -600,7 +610,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       uint2v vr[PD + 1][2];
       auto vread = [&](auto DTI) __attribute__((always_inline)) {
         constexpr int dt = decltype(DTI)::value;
-        constexpr int off = 256 * (dt >> 3) + 32 * hh * HD * 2;
+        constexpr int off = SOFF + 256 * (dt >> 3) + 32 * hh * HD * 2;
         vr[dt % (PD + 1)][0] = lds_tr_b64<off>(vaddr[dt & 7]);
         vr[dt % (PD + 1)][1] = lds_tr_b64<off + 4 * HD * 2>(vaddr[dt & 7]);
       };
@@ -846,6 +856,9 @@ SplitFn pick_shape(int nw, int tpw, int qmode, int mm) {
 // query registers.
 int max_tiles_per_wave(int hd, bool f16_query) {
   if (hd == 256) return 1;
+  // (hd 128 with the hi/lo pair fits two tiles too, but measured slower: the
+  // doubled rows per workgroup need twice the key splits to fill the machine,
+  // and the split partials grow with them)
   if (hd == 128) return f16_query ? 2 : 1;
   return 2;
 }
