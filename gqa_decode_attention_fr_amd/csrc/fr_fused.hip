@@ -365,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 
   // m_run: reference max in natural-log units; lacc: running row sums (all four
   // elements equal); o: unnormalised output tiles
-  float m_run[TPW], alpha[TPW];
+  float m_run[TPW], m_thr[TPW], nbv[TPW], alpha[TPW];
   float4v lacc[TPW];
   float4v o[TPW][DT];
   const half8 kOnes = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
@@ -373,6 +373,8 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     m_run[i] = -INFINITY;
+    m_thr[i] = -INFINITY;
+    nbv[i] = 0.f;
     alpha[i] = 1.f;
     lacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -439,15 +441,12 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
   // between stages, before the PV of the half that moved it.
   float yv[TPW][8];   // logits, then probabilities, of the half in flight
   float bmv[TPW];     // block max of the half in flight
-  float nbv[TPW];     // -m_run * log2(e) (0 while m_run = -inf)
   bool moved = false;
   half8 pb[TPW][2];   // P^T of the two halves, the PV B operand
 
   // Step ST (0..7) of the softmax of half HH for every tile of the wave.
   auto sm_step = [&](auto STEP, auto HH, bool ragged, const half8 (&mh)[TPW][2],
-                     const float4v (&sc)[TPW][4], const auto &sc2, int kb0)
-                     __attribute__((always_inline)) {
-    constexpr bool split_acc = sizeof(sc2[0]) == sizeof(sc[0]);   // 4 kt entries
+                     const float4v (&sc)[TPW][4], int kb0) __attribute__((always_inline)) {
     constexpr int st = decltype(STEP)::value;
     constexpr int hh = decltype(HH)::value;
 #pragma unroll
@@ -458,9 +457,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float m = MASKMODE != kMaskNone ? (float)mh[i][hh][4 * st + e] : 0.f;
-          float sv = sc[i][2 * hh + st][e];
-          if constexpr (split_acc) sv += sc2[i][2 * hh + st][e];
-          yv[i][4 * st + e] = fmaf(sv, a.scale, m);
+          yv[i][4 * st + e] = fmaf(sc[i][2 * hh + st][e], a.scale, m);
           pin(yv[i][4 * st + e]);
         }
         if (ragged) {   // uniform: only the block holding the split's end
@@ -485,15 +482,16 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
         const float bm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
         const float m_old = m_run[i];
         // moves when bm exceeds the reference by more than kLazy; also taken
-        // when m_old = -inf and bm is finite (alpha = 2^-inf = 0 then)
-        const bool mv = bm > m_old + kLazy;
-        const float al = fast_exp2((m_old - bm) * kLog2e);
-        alpha[i] = mv ? al : 1.f;
-        m_run[i] = mv ? bm : m_old;
-        moved = moved || mv;
-        nbv[i] = (m_run[i] == -INFINITY) ? 0.f : -m_run[i] * kLog2e;
-        pin(nbv[i]);
-        pin(alpha[i]);
+        // when m_old = -inf and bm is finite (alpha = 2^-inf = 0 then).  The
+        // common case costs one compare and a uniform branch.
+        const bool mv = bm > m_thr[i];   // m_thr = m_run + kLazy
+        if (__any(mv)) {                   // rare: the reference max moves
+          alpha[i] = mv ? fast_exp2((m_old - bm) * kLog2e) : 1.f;
+          m_run[i] = mv ? bm : m_old;
+          m_thr[i] = m_run[i] + kLazy;
+          nbv[i] = (m_run[i] == -INFINITY) ? 0.f : -m_run[i] * kLog2e;
+          moved = true;
+        }
       } else if constexpr (st <= 6) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -511,12 +509,13 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 
   // Output rescale after a half that moved some reference max.
   auto rescale = [&]() __attribute__((always_inline)) {
-    if (__any(moved)) {
+    if (moved) {   // wave-uniform
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[i][dt] *= alpha[i];
         lacc[i] *= alpha[i];
+        alpha[i] = 1.f;
       }
     }
     moved = false;
@@ -543,20 +542,11 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     };
     mread(std::integral_constant<int, 0>{});
 
-    // Score accumulators.  With one tile per wave the two K tiles of a half
-    // would give only two dependent MFMA chains; a second accumulator set
-    // (the lo query half, or odd ks for a single f16 operand) doubles that,
-    // and is added in when the scores are read.
-    constexpr bool kSplitAcc = TPW == 1 && HD <= 128;
-    constexpr int NSA = kSplitAcc ? 4 : 1;
-    float4v sc[TPW][4], sc2[TPW][NSA];
+    float4v sc[TPW][4];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
+    for (int i = 0; i < TPW; ++i)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) sc[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < NSA; ++kt) sc2[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
-    }
 
     // LDS prefetch distance (steps ahead) of the K and V fragment reads:
     // deeper where the register budget allows (one tile per wave, hd <= 128).
@@ -586,17 +576,8 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
           for (int i = 0; i < TPW; ++i) {
             const half8 kf = kb[ks % (PD + 1)][j];
-            if constexpr (kSplitAcc && QMODE == kQHiLo) {
-              sc[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc[i][2 * hh + j]);
-              sc2[i][2 * hh + j] = mfma16x16x32(kf, ql[i][ks], sc2[i][2 * hh + j]);
-            } else if constexpr (kSplitAcc) {
-              if constexpr (ks & 1) sc2[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc2[i][2 * hh + j]);
-              else sc[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc[i][2 * hh + j]);
-            } else {
-              sc[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc[i][2 * hh + j]);
-              if (QMODE == kQHiLo)
-                sc[i][2 * hh + j] = mfma16x16x32(kf, ql[i][ks], sc[i][2 * hh + j]);
-            }
+            sc[i][2 * hh + j] = mfma16x16x32(kf, qh[i][ks], sc[i][2 * hh + j]);
+            if (QMODE == kQHiLo) sc[i][2 * hh + j] = mfma16x16x32(kf, ql[i][ks], sc[i][2 * hh + j]);
           }
         }
         after(KSI);
@@ -651,7 +632,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       static_for<8>([&](auto STI) __attribute__((always_inline)) {
         constexpr int stp = decltype(STI)::value;
         if constexpr (stp * KS >= 8 * ks && stp * KS < 8 * (ks + 1))
-          sm_step(STI, H0{}, ragged, mh, sc, sc2, kb0);
+          sm_step(STI, H0{}, ragged, mh, sc, kb0);
       });
     });
     // (the last wait of stage B was lgkmcnt(0): the half-1 mask has landed)
@@ -666,7 +647,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       static_for<8>([&](auto STI) __attribute__((always_inline)) {
         constexpr int stp = decltype(STI)::value;
         if constexpr (stp * DT >= 8 * dt && stp * DT < 8 * (dt + 1))
-          sm_step(STI, H1{}, ragged, mh, sc, sc2, kb0);
+          sm_step(STI, H1{}, ragged, mh, sc, kb0);
       });
     });
     rescale();
