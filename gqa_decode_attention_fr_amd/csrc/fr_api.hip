@@ -22,7 +22,6 @@
 
 namespace fr {
 
-int max_tiles_per_wave(int hd, bool f16_query);  // fused split kernel register budget
 
 int env_int(const char *name, int fallback) {
   const char *s = std::getenv(name);
@@ -48,7 +47,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int kTargetWorkgroups = 256;
 
 int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flags,
-              bool f16_query, Plan *plan) {
+              Plan *plan) {
   Plan p;
   const int M = n_head * n_tok;
   p.variant = (flags & FR_VARIANT_DECOMPOSED) ? kDecomposed : kFused;
@@ -58,24 +57,27 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
     p.waves = 4;
     p.tiles = hd == 256 ? 1 : (hd == 128 ? 2 : 4);
   } else {
-    // split kernel: up to 4 tiles run as 4 waves x 1 tile (one wave per SIMD);
-    // larger row counts use 8 waves (two per SIMD, hiding each other's
-    // latency) with as many tiles per wave as the register budget allows
-    if (tiles_total <= 4) {
-      p.waves = 4;
-      p.tiles = 1;
-    } else {
-      p.waves = 8;
-      p.tiles = 1;
-      const int cap = max_tiles_per_wave(hd, f16_query);
-      while (p.tiles < cap && p.waves * p.tiles < tiles_total) p.tiles *= 2;
-    }
+    // split kernel: one 16-row tile per wave.  Up to 16 tiles run as row
+    // blocks of 4 waves (one per SIMD, 64 rows per workgroup): small row
+    // blocks keep each workgroup's query loads and partial stores short and
+    // spread the call over more compute units.  More rows use 8 waves (two per
+    // SIMD, hiding each other's latency), which halves how often the K/V
+    // blocks are staged per row.
+    p.waves = tiles_total <= 16 ? 4 : 8;
+    p.tiles = 1;
   }
-  const int tiles = p.tiles;
-  const int rows_per_wg = p.waves * tiles * 16;
+  const int rows_per_wg = p.waves * p.tiles * 16;
   p.n_rowblk = (int)cdiv(M, rows_per_wg);
   const int key_blocks = (int)cdiv(n_kv, kKeyBlock);
-  int want = (int)std::max<int64_t>(1, cdiv(kTargetWorkgroups, (int64_t)n_inst * p.n_rowblk));
+  // Key splits: as many as keep the grid within one workgroup per compute
+  // unit.  Where that leaves a single key block per split, two blocks per
+  // split are taken instead if the grid still covers half the machine: the
+  // partials (and their combine) then halve, and block 1 loads while block 0
+  // is computed.
+  const int64_t wg_per_split = (int64_t)n_inst * p.n_rowblk;
+  int want = (int)std::max<int64_t>(1, kTargetWorkgroups / wg_per_split);
+  if (cdiv(key_blocks, want) < 2 && wg_per_split * cdiv(key_blocks, 2) >= kTargetWorkgroups / 2)
+    want = (int)cdiv(key_blocks, 2);
   const int forced = env_int("FR_FORCE_SPLITS", 0);
   if (forced > 0) want = forced;
   want = std::min(std::max(want, 1), key_blocks);
@@ -232,8 +234,7 @@ int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const
   if (st != FR_OK) return st;
   if (n_inst == 1) q_stride = kv_stride = mask_stride = out_stride = 0;
   Plan plan;
-  const bool f16_query = q_format == FR_Q_F16 || (flags & FR_Q_ROUND_F16);
-  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, f16_query, &plan);
+  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &plan);
   if (st != FR_OK) return st;
   if (caller_ws) {
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
@@ -314,15 +315,9 @@ size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv
   if (st == FR_OK) st = check_flags(FR_Q_F32, flags);
   size_t need = 0;
   if (st == FR_OK) {
-    // the plan depends on the query precision; cover f16 queries too unless
-    // the flags already say the query is used at f16 precision
-    Plan a, b;
-    st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, true, &a);
-    if (st == FR_OK && !(flags & FR_Q_ROUND_F16))
-      st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, false, &b);
-    else
-      b = a;
-    need = std::max(a.ws_bytes, b.ws_bytes);
+    Plan a;
+    st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &a);
+    need = a.ws_bytes;
   }
   if (status) *status = st;
   return st == FR_OK ? need : 0;
@@ -344,7 +339,7 @@ int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, uns
   if (st == FR_OK) st = check_flags(FR_Q_F32, flags);
   if (st != FR_OK) return st;
   Plan p;
-  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, (flags & FR_Q_ROUND_F16) != 0, &p);
+  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &p);
   if (st != FR_OK) return st;
   const int vals[8] = {p.variant, p.n_split, p.chunk, p.waves,
                        p.tiles,   p.n_rowblk, p.grid, p.launches};

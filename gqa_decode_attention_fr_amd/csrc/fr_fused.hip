@@ -718,30 +718,37 @@ struct CombineArgs {
   int M, n_split, n_inst;
 };
 
-// One workgroup per (instance, row): 256 threads = G split groups x (HD/4)
-// columns of 4 consecutive d.  Thread (g, c) merges splits g, g+G, g+2G, ...
-// (all of its loads in flight together), then the G group results are merged
-// in group order through LDS.  With m the running max (log2 units):
+// 256 threads = RW rows x G split groups x (HD/4) columns of 4 consecutive d,
+// with G * RW * HD/4 = 256.  Thread (row, g, c) merges splits g, g+G, g+2G, ...
+// (R of its loads in flight together); with G > 1 the G group results of a row
+// are then merged in group order through LDS.  Few splits take G = 1 and several
+// rows per workgroup, so every load of a row is in flight at once and no LDS
+// merge is needed.  With m the running max (log2 units):
 //   out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s
 // A split with no visible key has m_s = -inf and weight 0; a row with no
 // visible key at all is written as zeros.  The merge order is fixed, so the
 // result does not depend on timing.
-template <int HD>
+template <int HD, int G>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int C = HD / 4;          // float4 columns per row
-  constexpr int G = 256 / C;         // split groups
+  constexpr int RW = 256 / (C * G);  // rows per workgroup
+  static_assert(RW >= 1 && RW * G * C == 256, "thread layout");
   constexpr int R = 8;               // loads in flight per thread per round
-  __shared__ float4v s_acc[G][C];
-  __shared__ float s_m[G][C], s_l[G][C];
+  __shared__ float4v s_acc[G > 1 ? RW : 1][G][C];
+  __shared__ float s_m[G > 1 ? RW : 1][G][C], s_l[G > 1 ? RW : 1][G][C];
 
-  const int c = threadIdx.x % C, g = threadIdx.x / C;
-  const int r = blockIdx.x % a.M;
-  const int inst = blockIdx.x / a.M;
+  const int c = threadIdx.x % C;
+  const int g = (threadIdx.x / C) % G;
+  const int rw = threadIdx.x / (C * G);
+  const int row = blockIdx.x * RW + rw;          // over n_inst * M
+  const bool on = row < a.n_inst * a.M;
+  const int r = on ? row % a.M : 0;
+  const int inst = on ? row / a.M : 0;
   const int64_t base = (int64_t)inst * a.n_split;
 
   float m = -INFINITY, l = 0.f;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = g; s0 < a.n_split; s0 += G * R) {
+  for (int s0 = g; on && s0 < a.n_split; s0 += G * R) {
     float2v ml[R];
     float4v po[R];
 #pragma unroll
@@ -770,26 +777,49 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
     m = mc;
   }
-  s_acc[g][c] = acc;
-  s_m[g][c] = m;
-  s_l[g][c] = l;
-  __syncthreads();
-  if (g != 0) return;
-  float mm = -INFINITY;
+  if constexpr (G > 1) {
+    s_acc[rw][g][c] = acc;
+    s_m[rw][g][c] = m;
+    s_l[rw][g][c] = l;
+    __syncthreads();
+    if (g != 0) return;
+    float mm = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < G; ++j) mm = fmaxf(mm, s_m[j][c]);
-  float4v out = {0.f, 0.f, 0.f, 0.f};
-  if (mm != -INFINITY) {
-    float ll = 0.f;
+    for (int j = 0; j < G; ++j) mm = fmaxf(mm, s_m[rw][j][c]);
+    acc = float4v{0.f, 0.f, 0.f, 0.f};
+    l = 0.f;
+    if (mm != -INFINITY) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float w = fast_exp2(s_m[j][c] - mm);
-      ll += w * s_l[j][c];
-      out += w * s_acc[j][c];
+      for (int j = 0; j < G; ++j) {
+        const float w = fast_exp2(s_m[rw][j][c] - mm);
+        l += w * s_l[rw][j][c];
+        acc += w * s_acc[rw][j][c];
+      }
     }
-    out *= 1.f / ll;
   }
+  if (!on) return;
+  const float4v out = (l > 0.f) ? acc * (1.f / l) : float4v{0.f, 0.f, 0.f, 0.f};
   *(float4v *)(a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD + 4 * c) = out;
+}
+
+// Split groups of the combine: enough that each thread has at most R = 8 splits
+// to load, and no more (more groups mean fewer rows per workgroup).
+template <int HD>
+hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
+  constexpr int C = HD / 4;
+  const int rows = c.n_inst * c.M;
+  auto go = [&](auto GI) {
+    constexpr int G = decltype(GI)::value < 256 / C ? decltype(GI)::value : 256 / C;
+    constexpr int RW = 256 / (C * G);
+    hipLaunchKernelGGL((combine_kernel<HD, G>), dim3((rows + RW - 1) / RW), dim3(256), 0, stream, c);
+    return hipGetLastError();
+  };
+  const int need = (c.n_split + 7) / 8;   // groups that give each thread <= 8 splits
+  if (need <= 1) return go(std::integral_constant<int, 1>{});
+  if (need <= 2) return go(std::integral_constant<int, 2>{});
+  if (need <= 4) return go(std::integral_constant<int, 4>{});
+  if (need <= 8) return go(std::integral_constant<int, 8>{});
+  return go(std::integral_constant<int, 16>{});
 }
 
 typedef void (*SplitFn)(SplitArgs);
@@ -814,35 +844,15 @@ SplitFn pick_q(int qmode, int mm) {
   }
 }
 
-// Instantiated shapes: 4 waves x 1 tile, 8 waves x 1 tile, and 8 waves x 2
-// tiles for hd 64 (any query mode) and hd 128 (single f16 query operand only:
-// the hi/lo pair does not fit the register budget there).
+// Instantiated shapes: 4 or 8 waves, one 16-row tile per wave.
 template <int HD>
 SplitFn pick_shape(int nw, int tpw, int qmode, int mm) {
   if (nw == 4 && tpw == 1) return pick_q<HD, 4, 1>(qmode, mm);
   if (nw == 8 && tpw == 1) return pick_q<HD, 8, 1>(qmode, mm);
-  if constexpr (HD == 64) {
-    if (nw == 8 && tpw == 2) return pick_q<HD, 8, 2>(qmode, mm);
-  } else if constexpr (HD == 128) {
-    if (nw == 8 && tpw == 2 && qmode == kQF16) return pick_mask<HD, 8, 2, kQF16>(mm);
-    if (nw == 8 && tpw == 2 && qmode == kQRound) return pick_mask<HD, 8, 2, kQRound>(mm);
-  }
   return nullptr;
 }
 
 }  // namespace
-
-// Most 16-row tiles one wave of an 8-wave workgroup (256 registers per lane)
-// carries without spilling; an f32 query split into hi/lo halves doubles the
-// query registers.
-int max_tiles_per_wave(int hd, bool f16_query) {
-  if (hd == 256) return 1;
-  // (hd 128 with the hi/lo pair fits two tiles too, but measured slower: the
-  // doubled rows per workgroup need twice the key splits to fill the machine,
-  // and the split partials grow with them)
-  if (hd == 128) return f16_query ? 2 : 1;
-  return 2;
-}
 
 hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hipStream_t stream) {
   int mm = kMaskNone;
@@ -901,13 +911,12 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   c.M = M;
   c.n_split = plan.n_split;
   c.n_inst = p.n_inst;
-  const int blocks = p.n_inst * M;   // one workgroup per output row
   switch (p.hd) {
-    case 64: hipLaunchKernelGGL(combine_kernel<64>, dim3(blocks), dim3(256), 0, stream, c); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(blocks), dim3(256), 0, stream, c); break;
-    case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3(blocks), dim3(256), 0, stream, c); break;
+    case 64: return launch_combine<64>(c, stream);
+    case 128: return launch_combine<128>(c, stream);
+    case 256: return launch_combine<256>(c, stream);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fr

@@ -48,11 +48,10 @@ int env_int(const char *name, int fallback);
 // Caller events recorded around the main kernel (null when timing is off).
 void profile_events(hipEvent_t *start, hipEvent_t *stop);
 
-// Chooses the variant and the work decomposition (pure host logic).
-// f16_query: the score contraction takes one f16 query operand (f16 input or
-// FR_Q_ROUND_F16) rather than the hi/lo pair of an f32 query.
+// Chooses the variant and the work decomposition (pure host logic; the same
+// for every query format).
 int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flags,
-              bool f16_query, Plan *plan);
+              Plan *plan);
 
 // Enqueue the fused split-KV path (split kernel, plus the combine kernel when
 // n_split > 1).  Returns hipSuccess or the launch error.

@@ -147,9 +147,7 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k,
 
 /* Device workspace bytes a call with these sizes and flags needs (0 if none),
  * or 0 with *status set when the sizes are rejected (status may be NULL).
- * The launch plan depends on whether the query enters the matrix cores as one
- * f16 operand (f16 queries, or FR_Q_ROUND_F16) or as an f32 hi/lo pair; without
- * FR_Q_ROUND_F16 in flags the size covers both, so it also suits
+ * The size does not depend on the query format, so it also suits
  * fr_decode_attn_q16 and FR_Q_F16 calls. */
 size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv,
                                      int hd, unsigned flags, int *status);
@@ -161,9 +159,9 @@ int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
                            unsigned flags);
 
 /*
- * The launch plan a call with these sizes would use, for tests and
- * benchmarks; pass FR_Q_ROUND_F16 in flags to get the plan of an f16-precision
- * query (f16 input or rounded f32).  Fills up to n_info ints of info[]:
+ * The launch plan a call with these sizes and flags would use (the same for
+ * every query format), for tests and benchmarks.  Fills up to n_info ints of
+ * info[]:
  *   [0] variant (1 fused, 2 decomposed)  [1] key splits per instance
  *   [2] keys per split                   [3] waves per workgroup
  *   [4] 16-row tiles per wave            [5] row blocks per instance

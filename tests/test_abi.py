@@ -123,30 +123,32 @@ def test_plan_covers_keys_and_rows(shape, flags):
     tiles_total = -(-M // 16)
     if flags:
         assert p["waves"] == 4 and p["tiles"] == {256: 1, 128: 2, 64: 4}[hd]
-    elif tiles_total <= 4:
-        assert p["waves"] == 4 and p["tiles"] == 1
     else:
-        assert p["waves"] == 8 and p["tiles"] in (1, 2, 4)
-        assert p["tiles"] <= {256: 1, 128: 1, 64: 2}[hd]
+        assert p["tiles"] == 1 and p["waves"] == (4 if tiles_total <= 16 else 8)
+        # one workgroup per compute unit at most, unless instances x row blocks exceed it
+        assert p["grid"] <= max(256, n_inst * p["n_rowblk"])
     ws = B.fr_decode_attn_workspace_size(*shape, flags)
     if flags == 0:
-        def fused_ws(pl):
-            rows = n_inst * pl["n_split"] * M
-            return 0 if pl["n_split"] == 1 else -(-(rows * hd * 4 + rows * 8) // 256) * 256
-        p16 = B.fr_decode_attn_plan(*shape, B.FR_Q_ROUND_F16)
-        assert ws == max(fused_ws(p), fused_ws(p16))
-        assert ws == B.fr_decode_attn_workspace_size(*shape, 0)
-        assert B.fr_decode_attn_workspace_size(*shape, B.FR_Q_ROUND_F16) == fused_ws(p16)
+        rows = n_inst * p["n_split"] * M
+        assert ws == (0 if p["n_split"] == 1 else -(-(rows * hd * 4 + rows * 8) // 256) * 256)
+        assert B.fr_decode_attn_plan(*shape, B.FR_Q_ROUND_F16) == p   # format-independent
+        assert B.fr_decode_attn_workspace_size(*shape, B.FR_Q_ROUND_F16) == ws
         assert p["launches"] == (1 if p["n_split"] == 1 else 2)
     else:
         assert ws >= n_inst * M * n_kv * 6 and p["launches"] >= 3
 
 
-def test_f16_queries_take_more_rows_per_workgroup_at_hd128():
-    hilo = B.fr_decode_attn_plan(1, 32, 16, 32768, 128, 0)
-    f16 = B.fr_decode_attn_plan(1, 32, 16, 32768, 128, B.FR_Q_ROUND_F16)
-    assert hilo["tiles"] == 1 and f16["tiles"] == 2
-    assert hilo["n_rowblk"] == 2 * f16["n_rowblk"]
+@pytest.mark.parametrize("shape,want", [
+    # (n_inst, n_head, n_tok, n_kv, hd) -> (waves, row blocks, splits, keys per split)
+    ((18, 8, 10, 1024, 256), (4, 2, 6, 192)),     # 36 row blocks: 7 splits fit, 3 blocks each
+    ((1, 16, 16, 4096, 128), (4, 4, 32, 128)),    # 1-block splits would be 256; 2 blocks keep 128
+    ((1, 8, 16, 2048, 256), (4, 2, 32, 64)),      # 2 blocks per split would leave 32 workgroups
+    ((1, 32, 16, 32768, 128), (8, 4, 64, 512)),   # 32 tiles: 8 waves, 256 workgroups
+    ((1, 8, 1, 64, 256), (4, 1, 1, 64)),
+])
+def test_plan_shapes(shape, want):
+    p = B.fr_decode_attn_plan(*shape, 0)
+    assert (p["waves"], p["n_rowblk"], p["n_split"], p["chunk"]) == want
 
 
 def test_forced_split_count(monkeypatch):
