@@ -66,8 +66,12 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
     p.waves = tiles_total <= 16 ? 4 : 8;
     p.tiles = 1;
   }
-  const int rows_per_wg = p.waves * p.tiles * 16;
-  p.n_rowblk = (int)cdiv(M, rows_per_wg);
+  // Row blocks of at most waves*tiles tiles, balanced: with 5 tiles and room
+  // for 4, blocks of 3 and 2 rather than 4 and 1 (the largest block sets the
+  // per-workgroup query loads and partial stores).
+  const int tiles_cap = p.waves * p.tiles;
+  p.n_rowblk = (int)cdiv(tiles_total, tiles_cap);
+  p.tpr = p.variant == kFused ? (int)cdiv(tiles_total, p.n_rowblk) : tiles_cap;
   const int key_blocks = (int)cdiv(n_kv, kKeyBlock);
   // Key splits: as many as keep the grid within one workgroup per compute
   // unit.  Where that leaves a single key block per split, two blocks per

@@ -64,6 +64,7 @@ struct SplitArgs {
   int64_t q_stride, kv_stride, mask_stride, out_stride;
   int n_head, n_tok, n_kv, M;
   int n_split, chunk, n_rowblk;
+  int tpr;          // 16-row tiles per row block (<= NW * TPW)
   float scale;      // applied to q.k before the mask
 };
 
@@ -90,6 +91,13 @@ __device__ __forceinline__ void pin(T &x) {
 // 16-byte global -> LDS copy: lane l's bytes land at lds_base + 16*l.
 __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
   __builtin_amdgcn_global_load_lds((global_cvoid *)g, (lds_void *)lds_base, 16, 0, 0);
+}
+// The same from a uniform base plus a 32-bit lane offset, as one load with a
+// scalar base register.  The offset passes through an empty statement so the
+// compiler cannot hoist a 64-bit per-lane sum out of the loop instead.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, void *lds_base) {
+  asm volatile("" : "+v"(off));
+  dma16(base + off, lds_base);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
@@ -192,7 +200,7 @@ struct Stage {
 
 // NW waves per workgroup (4 or 8), TPW 16-row tiles per wave.
 template <int HD, int NW, int TPW, int QMODE, int MASKMODE>
-__global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
+__global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   constexpr int kWaves = NW;
   constexpr int kThreads = NW * 64;
   constexpr int GPR = HD / 8;                 // 16-byte granules per K/V row
@@ -216,15 +224,26 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int l16 = lane & 15;
   const int g = lane >> 4;
 
-  int bid = blockIdx.x;
-  const int split = bid % a.n_split;
-  bid /= a.n_split;
-  const int rowblk = bid % a.n_rowblk;
-  const int inst = bid / a.n_rowblk;
+  // Workgroup -> (instance, key split, row block).  Workgroup b runs on XCD
+  // b % 8, and each XCD has its own L2: the row blocks of one (instance,
+  // split) pair read the same K/V chunk, so they take workgroups 8 apart (the
+  // same XCD, dispatched close together).  Pairs x = inst*n_split + split go
+  // in groups of 8 (fewer in the last group): group gr holds its pairs' row
+  // block 0, then row block 1, ...
+  const int n_pair = gridDim.x / a.n_rowblk;
+  const int gr = blockIdx.x / (8 * a.n_rowblk);
+  const int in_gr = blockIdx.x - gr * 8 * a.n_rowblk;
+  const int gcnt = min(8, n_pair - 8 * gr);
+  // (integer division runs on the vector unit; the results are uniform and
+  // are moved back to scalar registers, so addresses built from them are too)
+  const int rowblk = __builtin_amdgcn_readfirstlane(in_gr / gcnt);
+  const int pair = 8 * gr + in_gr - rowblk * gcnt;
+  const int split = __builtin_amdgcn_readfirstlane(pair % a.n_split);
+  const int inst = __builtin_amdgcn_readfirstlane(pair / a.n_split);
 
   const uint16_t *kbase = a.k + (int64_t)inst * a.kv_stride;
   const uint16_t *vbase = a.v + (int64_t)inst * a.kv_stride;
@@ -235,49 +254,49 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 
   uint16_t rm[2][NMR]; // register-staged mask values (kMaskReg only)
 
-  // Per-lane DMA source offsets (elements), fixed for the whole kernel.
-  // Granule lin = (wave*NJ + j)*64 + lane of a block is K/V row
-  // r = lin / GPR, 16-byte slot lin % GPR = lane % GPR; it lands at LDS slot
-  // slot ^ swz(r).  Only the block's first key moves between blocks.
+  // Per-lane DMA source byte offsets from the block's first K (V) row, fixed
+  // for the whole kernel.  Granule lin = (wave*NJ + j)*64 + lane of a block is
+  // K/V row r = lin / GPR, 16-byte slot lin % GPR = lane % GPR; it lands at
+  // LDS slot slot ^ swz(r).  Only the block's first key moves between blocks,
+  // and it is uniform: each load is a scalar base plus a 32-bit lane offset.
   constexpr int RPI = 64 / GPR;                       // rows per DMA instruction
-  int dma_kofs[NJ], dma_vofs[NJ], dma_row[NJ];
+  uint32_t dma_kofs[NJ], dma_vofs[NJ];
+  int dma_row[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int r = (wave * NJ + j) * RPI + lane / GPR;
     const int slot = lane % GPR;
     dma_row[j] = r;
-    dma_kofs[j] = r * HD + 8 * (slot ^ swz_k(r, GPR));
-    dma_vofs[j] = r * HD + 8 * (slot ^ swz_v(r, GPR));
+    dma_kofs[j] = 2u * (uint32_t)(r * HD + 8 * (slot ^ swz_k(r, GPR)));
+    dma_vofs[j] = 2u * (uint32_t)(r * HD + 8 * (slot ^ swz_v(r, GPR)));
   }
-  // mask granule of this lane: token t = lin / 8, key group (lin % 8) ^ swz_m(t)
+  // mask granule of this lane: token t = lin / 8, key group (lin % 8) ^ swz_m(t);
+  // byte offset < 2^31 (n_tok <= 16, n_kv <= 2^26)
   const int m_lin = wave * 64 + lane;
   const int m_tok = m_lin >> 3;
   const int m_gr = (m_lin & 7) ^ swz_m(m_lin >> 3);
-  const int m_ofs = m_tok < a.n_tok ? m_tok * a.n_kv + 8 * m_gr : 0;   // < 2^31
+  const uint32_t m_ofs = m_tok < a.n_tok ? 2u * (uint32_t)(m_tok * a.n_kv + 8 * m_gr) : 0u;
 
-  // Issue every load of one 64-key block into stage `s`.  Blocks that reach
-  // past n_kv (at most the last) clamp their rows to a valid one and read the
-  // mask granules past n_kv from a valid address (those keys are dropped by
-  // the ragged-block handling of the softmax).
+  // Issue every load of one 64-key block into stage `s`, in the order K,
+  // mask, V: the last NJ vector-memory operations of a wave are its V loads,
+  // so a wait for at most NJ outstanding operations has K and the mask.
+  // Blocks that reach past n_kv (at most the last) clamp their rows to a
+  // valid one and read the mask granules past n_kv from a valid address
+  // (those keys are dropped by the ragged-block handling of the softmax).
   auto issue = [&](Stage<HD, NW> &s, int kb0, uint16_t (&rmr)[NMR]) __attribute__((always_inline)) {
     const bool full = kb0 + KB <= a.n_kv;
-    const uint16_t *kb = kbase + (int64_t)kb0 * HD;
-    const uint16_t *vb = vbase + (int64_t)kb0 * HD;
+    const char *kb = (const char *)(kbase + (int64_t)kb0 * HD);   // uniform
+    const char *vb = (const char *)(vbase + (int64_t)kb0 * HD);
+    const int last = a.n_kv - 1 - kb0;                              // last valid row
+    uint32_t back[NJ];   // bytes from rows past n_kv back to the last key
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      int ko = dma_kofs[j], vo = dma_vofs[j];
-      if (!full) {
-        const int back = max(kb0 + dma_row[j] - (a.n_kv - 1), 0) * HD;   // rows past n_kv
-        ko -= back;
-        vo -= back;
-      }
-      dma16(kb + ko, (char *)s.k + (wave * NJ + j) * 1024);
-      dma16(vb + vo, (char *)s.v + (wave * NJ + j) * 1024);
+      back[j] = full ? 0u : 2u * (uint32_t)(max(dma_row[j] - last, 0) * HD);
+      dma16(kb, dma_kofs[j] - back[j], (char *)s.k + (wave * NJ + j) * 1024);
     }
     if (MASKMODE == kMaskDma) {
       const bool ok = m_tok < a.n_tok && (full || kb0 + 8 * m_gr < a.n_kv);
-      const uint16_t *src = ok ? mbase + (int64_t)kb0 + m_ofs : mbase;
-      dma16(src, (char *)s.m + wave * 1024);
+      dma16((const char *)mbase, ok ? 2u * (uint32_t)kb0 + m_ofs : 0u, (char *)s.m + wave * 1024);
     } else if (MASKMODE == kMaskReg) {
 #pragma unroll
       for (int i = 0; i < NMR; ++i) {
@@ -287,6 +306,9 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
         rmr[i] = mbase[ok ? (int64_t)t * a.n_kv + kb0 + j : 0];
       }
     }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      dma16(vb, dma_vofs[j] - back[j], (char *)s.v + (wave * NJ + j) * 1024);
   };
 
   // kMaskReg: place the register-staged values (after they have arrived).
@@ -299,12 +321,14 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     }
   };
 
-  // ---- query rows of this wave: tile i is tile (wave + 4i) of the row block
-  const int tile_base = rowblk * (kWaves * TPW) + wave;
-  // a wave with no row in range skips the arithmetic (it still loads and
-  // joins every barrier); inside a wave all TPW tiles are computed, rows past
-  // M carry zero queries and are never stored
-  const bool wave_on = tile_base * 16 < a.M;
+  // ---- query rows of this wave: tile i is tile (wave + kWaves*i) of the row
+  // block, which holds tiles rowblk*tpr .. rowblk*tpr + tpr - 1 (the planner
+  // balances the row blocks, so tpr may be below NW*TPW)
+  const int tile_base = rowblk * a.tpr + wave;
+  // a wave with no tile in the block or no row in range skips the arithmetic
+  // (it still loads and joins every barrier); inside a wave all TPW tiles are
+  // computed, rows past M or past the row block are never stored
+  const bool wave_on = wave < a.tpr && tile_base * 16 < a.M;
   // raw query values first; they are split into f16 operands only after the
   // first block has landed, so waiting on them never waits on the prefetch
   float4v qraw[TPW][KS][2];
@@ -335,11 +359,12 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 
   // The queries and block 0 first, alone: every workgroup starts at once, so
   // requesting block 1 as well would make block 0 (and the start of the
-  // arithmetic) wait behind the whole machine's block-1 traffic.  Block 1 is
-  // issued once block 0 has landed and loads while block 0 is computed.
+  // arithmetic) wait behind the whole machine's block-1 traffic.  The scores
+  // of block 0 start once the queries, K and the mask have landed; its V is
+  // waited for between the score and the PV stages, and block 1 is requested
+  // then (it loads while block 0 is computed).
   issue(st0, key_begin, rm[0]);
-  wait_vm<0>();
-  if (nblk > 1) issue(st1, key_begin + KB, rm[1]);
+  wait_vm<NJ>();
 
   half8 qh[TPW][KS], ql[TPW][KS];
 #pragma unroll
@@ -521,7 +546,9 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     moved = false;
   };
 
-  auto compute = [&](auto SI, int kb0) __attribute__((always_inline)) {
+  // Called by every wave (a wave without rows skips the arithmetic but joins
+  // the barrier of the first block).
+  auto compute = [&](auto SI, int kb0, bool first) __attribute__((always_inline)) {
     constexpr int si = decltype(SI)::value;
     const bool ragged = kb0 + KB > key_end;
     constexpr int asi = kImmStage ? 0 : si;              // lane address set
@@ -618,6 +645,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
 
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
+    if (wave_on) {
     // A
     qk_half(H0{}, [&](auto) __attribute__((always_inline)) {});
     // (the last wait of stage A was lgkmcnt(0): the half-0 mask has landed)
@@ -641,6 +669,13 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       for (int i = 0; i < TPW; ++i) wait_lgkm_tie<0>(mh[i][1]);
     }
     rescale();
+    }
+    if (first) {   // uniform: block 0's V, then the request for block 1
+      wait_vm<0>();
+      barrier();
+      if (nblk > 1) issue(st1, key_begin + KB, rm[1]);
+    }
+    if (wave_on) {
     // C: softmax steps of half 1 after PV step dt of half 0
     pv_half(H0{}, [&](auto DTI) __attribute__((always_inline)) {
       constexpr int dt = decltype(DTI)::value;
@@ -653,20 +688,22 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     rescale();
     // D
     pv_half(H1{}, [&](auto) __attribute__((always_inline)) {});
+    }
   };
 
 
   // ---- main loop: two blocks per trip, st0 then st1.  Invariant at the top
-  // of a trip: block b is complete in st0 and only block b+1 (into st1) may
-  // still be in flight, so reads of st0 never wait on the prefetch; the wait
-  // for the next block is taken at the point it is needed.
+  // of a trip: block b is complete in st0 (for b = 0: all but its V) and only
+  // block b+1 (into st1) may still be in flight, so reads of st0 never wait on
+  // the prefetch; the wait for the next block is taken at the point it is
+  // needed.
   for (int b = 0; b < nblk; b += 2) {
     if (MASKMODE == kMaskReg) {
       place_mask(st0, rm[0]);
       wait_lgkm<0>();
     }
     barrier();
-    if (wave_on) compute(std::integral_constant<int, 0>{}, key_begin + b * KB);
+    compute(std::integral_constant<int, 0>{}, key_begin + b * KB, b == 0);
     barrier();
     if (b + 2 < nblk) issue(st0, key_begin + (b + 2) * KB, rm[0]);
     if (b + 1 >= nblk) break;
@@ -676,7 +713,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
       wait_lgkm<0>();
     }
     barrier();
-    if (wave_on) compute(std::integral_constant<int, 1>{}, key_begin + (b + 1) * KB);
+    compute(std::integral_constant<int, 1>{}, key_begin + (b + 1) * KB, false);
     barrier();
     if (b + 3 < nblk) {
       issue(st1, key_begin + (b + 3) * KB, rm[1]);
@@ -692,7 +729,7 @@ __global__ __launch_bounds__(NW * 64, 1) void split_kernel(SplitArgs a) {
     if (!wave_on) break;
     const float l = lacc[i][0];
     const int r = (tile_base + kWaves * i) * 16 + l16;
-    if (r >= a.M) continue;
+    if (r >= a.M || wave + kWaves * i >= a.tpr) continue;
     if (a.n_split == 1) {
       const float inv = (l > 0.f) ? 1.f / l : 0.f;
       float *orow = a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD;
@@ -887,6 +924,7 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   a.n_split = plan.n_split;
   a.chunk = plan.chunk;
   a.n_rowblk = plan.n_rowblk;
+  a.tpr = plan.tpr;
   a.scale = p.scale;
   const size_t part_o_bytes = (size_t)p.n_inst * plan.n_split * M * p.hd * sizeof(float);
   a.part_o = plan.n_split > 1 ? (float *)workspace : nullptr;

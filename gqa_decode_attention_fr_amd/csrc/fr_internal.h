@@ -23,6 +23,7 @@ struct Plan {
   int waves = 4;       // waves per workgroup of the split kernel
   int tiles = 1;       // 16-row tiles per wave
   int n_rowblk = 1;    // row blocks per instance
+  int tpr = 1;         // 16-row tiles per row block (balanced; <= waves * tiles)
   int grid = 0;        // workgroups of the split kernel
   int launches = 1;    // kernel launches per call
   size_t ws_bytes = 0; // device workspace bytes
