@@ -65,6 +65,8 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
     // blocks are staged per row.
     p.waves = tiles_total <= 16 ? 4 : 8;
     p.tiles = 1;
+    const int fw = env_int("FR_FORCE_WAVES", 0);   // developer knob (tests, A/B timing)
+    if (fw == 4 || fw == 8) p.waves = fw;
   }
   // Row blocks of at most waves*tiles tiles, balanced: with 5 tiles and room
   // for 4, blocks of 3 and 2 rather than 4 and 1 (the largest block sets the

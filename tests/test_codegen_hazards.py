@@ -1,0 +1,132 @@
+"""Compiled-code check for one matrix-core hazard in the split kernels.
+
+A vector-ALU instruction that reads the result of a v_mfma must issue a
+number of wait states after it.  The compiler pads this inside a basic block,
+but a read placed right after a taken branch (for instance the uniform
+ragged-block branch of the softmax) has been seen to get no padding and to
+read a stale accumulator.  This test compiles the fused kernels to gfx950
+assembly and checks every branch: MFMA results written in the instructions
+before a branch must not be read at its target sooner than the distance the
+compiler itself keeps within blocks.  Pure host work (no GPU).
+"""
+import collections
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from gqa_decode_attention_fr_amd import build as B
+
+SRC = os.path.join(B.CSRC, "fr_fused.hip")
+
+
+def _regs(text):
+    out = set()
+    for m in re.finditer(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b", text):
+        if m.group(3):
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def _wait_states(line):
+    m = re.match(r"s_nop (\d+)", line)
+    return int(m.group(1)) + 1 if m else 1
+
+
+def _sources(line):
+    """VGPRs an instruction reads (destination dropped for ALU ops and loads)."""
+    parts = line.split(None, 1)
+    ops = parts[1].split(",") if len(parts) > 1 else []
+    if line.startswith(("v_", "ds_read", "global_load", "buffer_load")):
+        ops = ops[1:]
+    return _regs(",".join(ops))
+
+
+def _functions(asm):
+    for name, body in re.findall(r"^(_ZN2fr\S*split_kernel\S*):[^\n]*\n(.*?)\.Lfunc_end", asm,
+                                 re.S | re.M):
+        lines = [l.strip() for l in body.splitlines()
+                 if (l.startswith("\t") and not l.strip().startswith((".", ";")))
+                 or l.startswith(".LBB")]
+        yield name, lines
+
+
+def _within_block_minimum(funcs):
+    """Smallest distance the compiler leaves between an MFMA and a VALU read
+    of its result inside one basic block."""
+    seen = collections.Counter()
+    for _, lines in funcs:
+        for i, l in enumerate(lines):
+            if not l.startswith("v_mfma"):
+                continue
+            dst = _regs(l.split()[1].rstrip(","))
+            ws = 0
+            for lk in lines[i + 1:i + 40]:
+                if lk.startswith((".LBB", "s_cbranch", "s_branch")):
+                    break
+                if lk.startswith("v_") and not lk.startswith("v_mfma"):
+                    if _sources(lk) & dst:
+                        seen[ws] += 1
+                        break
+                    if _regs(lk.split(None, 1)[1].split(",")[0]) & dst:
+                        break
+                if lk.startswith("v_mfma") and _regs(lk.split()[1].rstrip(",")) & dst:
+                    break
+                ws += _wait_states(lk)
+    return min(seen) if seen else None
+
+
+def _violations(funcs, need):
+    bad = []
+    for name, lines in funcs:
+        labels = {l.split(":")[0]: i for i, l in enumerate(lines) if l.startswith(".LBB")}
+        for i, l in enumerate(lines):
+            m = re.match(r"s_cbranch_\w+\s+(\.LBB\S+)|s_branch\s+(\.LBB\S+)", l)
+            if not m:
+                continue
+            pend, ws = [], 0
+            for j in range(i - 1, max(i - 24, -1), -1):
+                if lines[j].startswith(".LBB"):
+                    break
+                if lines[j].startswith("v_mfma"):
+                    pend.append((_regs(lines[j].split()[1].rstrip(",")), ws))
+                ws += _wait_states(lines[j])
+            if not pend:
+                continue
+            ws2 = 1  # the branch
+            for lk in lines[labels[m.group(1) or m.group(2)] + 1:]:
+                if lk.startswith(".LBB"):
+                    continue
+                if not lk.startswith(("v_mfma", "s_")):
+                    src = _sources(lk)
+                    for regs, w0 in pend:
+                        if regs & src and w0 + ws2 < need:
+                            bad.append(f"{name}: '{lk}' {w0 + ws2} wait states after its MFMA")
+                ws2 += _wait_states(lk)
+                if ws2 >= need:
+                    break
+    return bad
+
+
+@pytest.fixture(scope="module")
+def fused_asm(tmp_path_factory):
+    cc = B.hipcc()
+    if not shutil.which(cc) and not os.path.exists(cc):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "fr_fused.s"
+    subprocess.run([cc, *B.compile_flags(), "--cuda-device-only", "-S", SRC, "-o", str(out)],
+                   check=True, capture_output=True)
+    return out.read_text()
+
+
+def test_no_mfma_result_read_right_after_a_branch(fused_asm):
+    funcs = list(_functions(fused_asm))
+    assert len(funcs) >= 9, "split kernels not found in the assembly"
+    need = _within_block_minimum(funcs)
+    assert need is not None and need >= 4
+    bad = _violations(funcs, need)
+    assert not bad, "\n".join(bad[:10])

@@ -101,6 +101,35 @@ def test_random_shapes(oracle_mod, shape, variant):
         assert np.array_equal(got[0, 0], np.zeros((n_head, hd), dtype=np.float32))
 
 
+FORCED_WAVES = [  # n_head, n_tok, n_kv, hd, q dtype, mask kind, waves (the other count than planned)
+    (8, 10, 1000, 256, "f32", "random", 8),
+    (20, 16, 700, 256, "f32", "random", 4),    # M = 320: 20 tiles, planned as 8 waves
+    (20, 16, 700, 256, "f16", "none", 4),
+    (16, 16, 4096, 128, "f16", "zero", 8),
+    (64, 16, 2048, 128, "f32", "random", 4),
+    (9, 5, 333, 64, "f16", "random", 8),
+    (3, 16, 129, 128, "f32", "full_row", 8),
+]
+
+
+@pytest.mark.parametrize("shape", FORCED_WAVES, ids=lambda s: "h{}_t{}_kv{}_d{}_{}_{}_w{}".format(*s))
+def test_forced_wave_counts(oracle_mod, shape, monkeypatch):
+    """Both instantiated workgroup shapes (4 and 8 waves) against the oracle,
+    on shapes whose plan would pick the other one."""
+    import gqa_decode_attention_fr_amd as F
+    n_head, n_tok, n_kv, hd, qd, mk, waves = shape
+    say(f"forced waves {shape}")
+    monkeypatch.setenv("FR_FORCE_WAVES", str(waves))
+    assert F.fr_decode_attn_plan(1, n_head, n_tok, n_kv, hd)["waves"] == waves
+    c = W.random_case(FORCED_WAVES.index(shape) + 300, n_head, n_tok, n_kv, hd, q_dtype=qd,
+                      mask_kind=mk)
+    scale = 1.0 / math.sqrt(hd)
+    got = run_gpu(c, n_head, n_tok, n_kv, hd, scale, q_f16=(qd == "f16"), torch=torch)
+    want = oracle_instances(oracle_mod, c, n_head, n_tok, n_kv, hd, scale,
+                            oracle_mod.Q_F16 if qd == "f16" else oracle_mod.Q_F32)
+    assert_close(got, want, str(shape))
+
+
 @pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
 def test_round_f16_flag_matches_oracle(oracle_mod, variant):
     w = W.CAUSAL_TAIL
