@@ -576,8 +576,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       for (int kt = 0; kt < 4; ++kt) sc[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
 
     // LDS prefetch distance (steps ahead) of the K and V fragment reads:
-    // deeper where the register budget allows (one tile per wave, hd <= 128).
-    constexpr int PD = (HD <= 128 && TPW == 1) ? 2 : 1;
+    // deeper where the register budget allows (one tile per wave; at hd 256
+    // only with one wave per SIMD).  Measured: 2 beats 1 at hd 256 (one wave
+    // per SIMD waits on each step's reads otherwise); 3 does not beat 2.
+    constexpr int PD = (TPW == 1 && (HD <= 128 || NW == 4)) ? 2 : 1;
 
     // S^T for half HH: K tiles kt = 2HH, 2HH+1 (keys 32HH + 8g + 4(kt%2) + 0..3
     // in lane group g), fragments read PD steps ahead of their MFMAs.
