@@ -339,11 +339,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   for (int i = 0; i < TPW; ++i) {
     const int tile = tile_base + kWaves * i;
     const int r = tile * 16 + l16;
+    const bool in_blk = wave + kWaves * i < a.tpr;   // tile belongs to this row block
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int64_t off = (int64_t)r * HD + ks * 32 + g * 8;
       float4v x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-      if (r < a.M) {
+      if (r < a.M && in_blk) {
         if (QMODE == kQF16) {
           x0 = __builtin_bit_cast(float4v, *(const uint4v *)((const uint16_t *)qinst + off));
         } else {
@@ -798,7 +799,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       if (sp < a.n_split) {
         const int64_t prow = (base + sp) * a.M + r;
         ml[j] = a.part_ml[prow];
-        po[j] = *(const float4v *)(a.part_o + prow * HD + 4 * c);
+        // streaming loads: each partial is read once
+        po[j] = __builtin_nontemporal_load((const float4v *)(a.part_o + prow * HD + 4 * c));
       }
     }
     float mc = m;
