@@ -840,7 +840,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
   if (!on) return;
   const float4v out = (l > 0.f) ? acc * (1.f / l) : float4v{0.f, 0.f, 0.f, 0.f};
-  *(float4v *)(a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD + 4 * c) = out;
+  // streaming store: the output is not read again by this call
+  __builtin_nontemporal_store(out, (float4v *)(a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD + 4 * c));
 }
 
 // Split groups of the combine: enough that each thread has at most R = 8 splits
