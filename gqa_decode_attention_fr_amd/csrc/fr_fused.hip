@@ -100,11 +100,27 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t off, void *lds_
   dma16(base + off, lds_base);
 }
 
+// 16-byte global load issued as inline assembly: the compiler then inserts no
+// wait of its own for the result (it would wait for every outstanding load,
+// including the block loads issued after it).  The caller waits with
+// wait_vm_tie before anything reads the value.
+__device__ __forceinline__ float4v gload16(const void *p) {
+  float4v r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// The same, tied to values loaded with gload16 (they cannot be read before it).
+template <int N>
+__device__ __forceinline__ void wait_vm_tie(float4v &x, float4v &y) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
 }
 
 // Workgroup barrier that orders LDS accesses in the compiler without waiting
@@ -332,6 +348,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   // raw query values first; they are split into f16 operands only after the
   // first block has landed, so waiting on them never waits on the prefetch
   float4v qraw[TPW][KS][2];
+  bool q_on[TPW];
   const void *qinst = (QMODE == kQF16)
                           ? (const void *)((const uint16_t *)a.q + (int64_t)inst * a.q_stride)
                           : (const void *)((const float *)a.q + (int64_t)inst * a.q_stride);
@@ -340,50 +357,67 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     const int tile = tile_base + kWaves * i;
     const int r = tile * 16 + l16;
     const bool in_blk = wave + kWaves * i < a.tpr;   // tile belongs to this row block
+    q_on[i] = r < a.M && in_blk;
+    // every lane loads (rows out of range read row 0 and are zeroed after the wait)
+    const int64_t rbase = q_on[i] ? (int64_t)r * HD : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int64_t off = (int64_t)r * HD + ks * 32 + g * 8;
-      float4v x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-      if (r < a.M && in_blk) {
-        if (QMODE == kQF16) {
-          x0 = __builtin_bit_cast(float4v, *(const uint4v *)((const uint16_t *)qinst + off));
-        } else {
-          x0 = *(const float4v *)((const float *)qinst + off);
-          x1 = *(const float4v *)((const float *)qinst + off + 4);
-        }
+      const int64_t off = rbase + ks * 32 + g * 8;
+      if (QMODE == kQF16) {
+        qraw[i][ks][0] = gload16((const uint16_t *)qinst + off);
+        qraw[i][ks][1] = float4v{0.f, 0.f, 0.f, 0.f};
+      } else {
+        qraw[i][ks][0] = gload16((const float *)qinst + off);
+        qraw[i][ks][1] = gload16((const float *)qinst + off + 4);
       }
-      qraw[i][ks][0] = x0;
-      qraw[i][ks][1] = x1;
     }
   }
   asm volatile("" ::: "memory"); // query loads are issued before the block loads
 
   // The queries and block 0 first, alone: every workgroup starts at once, so
   // requesting block 1 as well would make block 0 (and the start of the
-  // arithmetic) wait behind the whole machine's block-1 traffic.  The scores
-  // of block 0 start once the queries, K and the mask have landed; its V is
-  // waited for between the score and the PV stages, and block 1 is requested
-  // then (it loads while block 0 is computed).
+  // arithmetic) wait behind the whole machine's block-1 traffic.  The queries
+  // land first (they were requested first) and are split into f16 operands
+  // while block 0 is still arriving; the scores of block 0 start once K and
+  // the mask have landed; its V is waited for between the score and the PV
+  // stages, and block 1 is requested then (it loads while block 0 is
+  // computed).
   issue(st0, key_begin, rm[0]);
-  wait_vm<NJ>();
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) wait_vm_tie<J>(qraw[i][ks][0], qraw[i][ks][1]);
+  }
 
   half8 qh[TPW][KS], ql[TPW][KS];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      float4v x0 = qraw[i][ks][0], x1 = qraw[i][ks][1];
-      asm volatile("" : "+v"(x0), "+v"(x1)); // keep the split after the wait above
+      const float4v zero = {0.f, 0.f, 0.f, 0.f};
+      const float4v x0 = q_on[i] ? qraw[i][ks][0] : zero;
+      const float4v x1 = q_on[i] ? qraw[i][ks][1] : zero;
       if (QMODE == kQF16) {
         qh[i][ks] = __builtin_bit_cast(half8, x0);
         ql[i][ks] = half8{};
       } else {
+        // pairs: hi = f16(x) (round to nearest even, packed), lo = f16(x - hi)
+        // with the difference taken exactly in one mixed-precision fma
         const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const _Float16 h = (_Float16)x[e]; // round to nearest even
-          qh[i][ks][e] = h;
-          ql[i][ks][e] = (QMODE == kQHiLo) ? (_Float16)(x[e] - (float)h) : (_Float16)0.f;
+        for (int e = 0; e < 8; e += 2) {
+          const half2v h = __builtin_convertvector(float2v{x[e], x[e + 1]}, half2v);
+          qh[i][ks][e] = h.x;
+          qh[i][ks][e + 1] = h.y;
+          if (QMODE == kQHiLo) {
+            const float2v r = {fmaf((float)h.x, -1.f, x[e]), fmaf((float)h.y, -1.f, x[e + 1])};
+            const half2v lo = __builtin_convertvector(r, half2v);
+            ql[i][ks][e] = lo.x;
+            ql[i][ks][e + 1] = lo.y;
+          } else {
+            ql[i][ks][e] = (_Float16)0.f;
+            ql[i][ks][e + 1] = (_Float16)0.f;
+          }
         }
       }
     }
@@ -454,6 +488,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       }
     }
   }
+
+  // block 0's K and mask (its V may still be in flight)
+  wait_vm<NJ>();
 
   // ---- one 64-key block, as a software pipeline over its two 32-key halves.
   // The MFMA work of one half runs while the softmax (VALU) of the other half
