@@ -110,6 +110,13 @@ __device__ __forceinline__ float4v gload16(const void *p) {
   return r;
 }
 
+// 2-byte global load (zero-extended), inline assembly for the same reason.
+__device__ __forceinline__ uint32_t gload_u16(const void *p) {
+  uint32_t r;
+  asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -268,7 +275,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   const int key_end = min(key_begin + a.chunk, a.n_kv);
   const int nblk = (key_end - key_begin + KB - 1) / KB;
 
-  uint16_t rm[2][NMR]; // register-staged mask values (kMaskReg only)
+  // register-staged mask values (kMaskReg only), loaded by inline assembly
+  // and read only after the wait for their block
+  uint32_t rm[2][NMR];
 
   // Per-lane DMA source byte offsets from the block's first K (V) row, fixed
   // for the whole kernel.  Granule lin = (wave*NJ + j)*64 + lane of a block is
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   // Blocks that reach past n_kv (at most the last) clamp their rows to a
   // valid one and read the mask granules past n_kv from a valid address
   // (those keys are dropped by the ragged-block handling of the softmax).
-  auto issue = [&](Stage<HD, NW> &s, int kb0, uint16_t (&rmr)[NMR]) __attribute__((always_inline)) {
+  auto issue = [&](Stage<HD, NW> &s, int kb0, uint32_t (&rmr)[NMR]) __attribute__((always_inline)) {
     const bool full = kb0 + KB <= a.n_kv;
     const char *kb = (const char *)(kbase + (int64_t)kb0 * HD);   // uniform
     const char *vb = (const char *)(vbase + (int64_t)kb0 * HD);
@@ -319,7 +328,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
         const int u = tid + i * kThreads;            // 1024 = 16 tokens x 64 keys
         const int t = u >> 6, j = u & 63;
         const bool ok = t < a.n_tok && kb0 + j < a.n_kv;
-        rmr[i] = mbase[ok ? (int64_t)t * a.n_kv + kb0 + j : 0];
+        rmr[i] = gload_u16(mbase + (ok ? (int64_t)t * a.n_kv + kb0 + j : 0));
       }
     }
 #pragma unroll
@@ -328,12 +337,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   };
 
   // kMaskReg: place the register-staged values (after they have arrived).
-  auto place_mask = [&](Stage<HD, NW> &s, const uint16_t (&rmr)[NMR]) __attribute__((always_inline)) {
+  // (called after the wait for the block; the empty statements keep every read
+  // of the loaded registers after it)
+  auto place_mask = [&](Stage<HD, NW> &s, uint32_t (&rmr)[NMR]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NMR; ++i) asm volatile("" : "+v"(rmr[i]));
 #pragma unroll
     for (int i = 0; i < NMR; ++i) {
       const int u = tid + i * kThreads;
       const int t = u >> 6, j = u & 63;
-      s.m[(t * 8 + ((j >> 3) ^ swz_m(t))) * 8 + (j & 7)] = rmr[i];
+      s.m[(t * 8 + ((j >> 3) ^ swz_m(t))) * 8 + (j & 7)] = (uint16_t)rmr[i];
     }
   };
 

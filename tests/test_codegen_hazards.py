@@ -1,4 +1,6 @@
-"""Compiled-code check for one matrix-core hazard in the split kernels.
+"""Compiled-code checks of the split kernels (gfx950 assembly, no GPU).
+
+1. A matrix-core read hazard.
 
 A vector-ALU instruction that reads the result of a v_mfma must issue a
 number of wait states after it.  The compiler pads this inside a basic block,
@@ -7,7 +9,14 @@ ragged-block branch of the softmax) has been seen to get no padding and to
 read a stale accumulator.  This test compiles the fused kernels to gfx950
 assembly and checks every branch: MFMA results written in the instructions
 before a branch must not be read at its target sooner than the distance the
-compiler itself keeps within blocks.  Pure host work (no GPU).
+compiler itself keeps within blocks.
+
+2. Explicit load waits.  The query and register-staged mask loads are inline
+assembly waited for with explicit vmcnt counts, because the compiler's own
+wait for them would also wait for the block loads issued after them.  The
+compiler therefore cannot protect their registers: this check simulates the
+in-order vmcnt queue along each kernel and fails if any instruction touches a
+register whose load may still be outstanding.
 """
 import collections
 import os
@@ -129,4 +138,39 @@ def test_no_mfma_result_read_right_after_a_branch(fused_asm):
     need = _within_block_minimum(funcs)
     assert need is not None and need >= 4
     bad = _violations(funcs, need)
+    assert not bad, "\n".join(bad[:10])
+
+
+def _outstanding_register_uses(funcs):
+    bad = []
+    for name, lines in funcs:
+        queue = []   # destination registers of outstanding vector-memory operations
+        for l in lines:
+            if l.startswith(".LBB"):
+                continue
+            op = l.split()[0]
+            m = re.match(r"s_waitcnt.*vmcnt\((\d+)\)", l)
+            if m:
+                del queue[:max(0, len(queue) - int(m.group(1)))]
+                continue
+            if op == "s_endpgm":
+                break
+            ops = l.split(None, 1)[1] if len(l.split(None, 1)) > 1 else ""
+            pending = set().union(*queue) if queue else set()
+            if op.startswith(("global_load", "buffer_load")) and "lds" not in op:
+                if _regs(ops) & pending:
+                    bad.append(f"{name}: '{l}'")
+                queue.append(_regs(ops.split(",")[0]))
+            elif op.startswith(("global_load_lds", "global_store", "buffer_store", "global_atomic")):
+                if _regs(ops) & pending:
+                    bad.append(f"{name}: '{l}'")
+                queue.append(set())
+            elif op.startswith(("v_", "ds_")) and _regs(ops) & pending:
+                bad.append(f"{name}: '{l}'")
+    return bad
+
+
+def test_no_register_use_before_its_load_wait(fused_asm):
+    funcs = list(_functions(fused_asm))
+    bad = _outstanding_register_uses(funcs)
     assert not bad, "\n".join(bad[:10])
