@@ -12,12 +12,13 @@
 // run inside one kernel per key split, so scores and probabilities never
 // leave the chip:
 //
-//   workgroup = 4 waves = (instance, row block, key split)
+//   workgroup = 4 or 8 waves = (instance, row block, key split); one 16-row
+//   query tile per wave
 //   K, V and mask blocks of 64 keys stream global -> LDS with gfx950's 16-byte
 //   direct-to-LDS loads (no register staging) into a two-stage ring, so block
 //   b+1 is in flight while block b is computed.  Waits are explicit vmcnt
 //   counts ahead of a plain s_barrier.
-//   each wave, for its 16-row tiles (tile i of wave w is tile w + 4i):
+//   each wave, for its tile:
 //     S^T = K . Q^T       v_mfma_f32_16x16x32_f16, fp32 accumulation; an f32 Q
 //                         enters as hi + lo f16 halves (two MFMAs)
 //     online softmax      scale*log2(e) folded in, exp2, block max shared by
