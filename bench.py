@@ -115,6 +115,29 @@ def make_call(F, w, pool, flags):
     return call
 
 
+def make_single_calls(F, w, pool, flags):
+    """The same batch as n_inst back-to-back single-instance calls."""
+    fmt = F.FR_Q_F16 if w.q_dtype == "f16" else F.FR_Q_F32
+    M = w.M
+    lib = F.binding.load()
+    qe = 2 if w.q_dtype == "f16" else 4
+    steps = (M * w.hd * qe, w.n_kv * w.hd * 2, w.n_kv * w.hd * 2, w.n_tok * w.n_kv * 2,
+             M * w.hd * 4)
+    ptrs = [(pool.q[r].data_ptr(), pool.k[r].data_ptr(), pool.v[r].data_ptr(),
+             pool.mask[r].data_ptr(), pool.out[r].data_ptr()) for r in range(pool.R)]
+
+    def call(slot, stream):
+        base = ptrs[slot]
+        for i in range(w.n_inst):
+            q, k, v, m, o = (b + i * d for b, d in zip(base, steps))
+            st = lib.fr_decode_attn_ex(q, fmt, k, v, m, o, 1, 0, 0, 0, 0, w.n_head, w.n_tok,
+                                       w.n_kv, w.hd, w.scale, flags, None, 0, stream)
+            if st != 0:
+                raise F.FrError(st, "fr_decode_attn_ex")
+
+    return call
+
+
 def sleep_cycles_for(torch, ms: float) -> int:
     """Calibrate torch.cuda._sleep (a bounded spin kernel) to about `ms`."""
     cycles = 1_000_000
@@ -162,6 +185,50 @@ def timed_region(torch, F, call, R, steps, stream_handle, same_slot=False, hook=
     ms_total = t0.elapsed_time(t1)
     kern = [a.elapsed_time(b) for a, b in zip(starts, stops)]
     return ms_total / steps, kern
+
+
+def graph_region(torch, call, R, steps):
+    """The same K calls captured once into a HIP graph (the way a serving loop
+    replays a decode step) and replayed behind a GPU sleep; ms per call."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            h = int(s.cuda_stream)
+            for i in range(steps):
+                call(i % R, h)
+    torch.cuda.current_stream().wait_stream(s)
+    graph.replay()                      # the first replay uploads the graph
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(sleep_cycles_for(torch, 20.0))
+    t0.record()
+    graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del graph
+    return ms
+
+
+def achievable_copy_gbps(torch, reps=20):
+    """Read+write bytes per second of a plain 256 MiB device copy (larger than
+    the MALL), the practical ceiling next to the 8 TB/s data-sheet peak."""
+    n = 64 << 20
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n * 4 * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del src, dst
+    return gbps
 
 
 def traffic_for(w_name: str, variant: int):
@@ -250,6 +317,16 @@ def run_workload(args, torch, F, W, w):
         "algorithmic_bytes": alg,
         "flops": w.flops(),
     }
+    ms_graph = graph_region(torch, call, pool.R, args.steps)
+    aux["graph_replayed_us_per_call"] = round(ms_graph * 1e3, 3)
+    if w.n_inst > 1:
+        singles = make_single_calls(F, w, pool, flags)
+        n_b = max(1, args.steps // 10)
+        ms_single, _ = timed_region(torch, F, singles, pool.R, n_b, stream, hook=False)
+        aux["single_instance_calls_us_per_batch"] = round(ms_single * 1e3, 3)
+    copy_gbps = achievable_copy_gbps(torch)
+    aux["achievable_copy_GBps"] = round(copy_gbps, 1)
+    aux["kernel_frac_of_achievable_copy"] = round(achieved / copy_gbps, 4)
     if args.warm:
         ms_warm, kern_warm = timed_region(torch, F, call, pool.R, args.steps, stream,
                                           same_slot=True)
