@@ -148,19 +148,22 @@ def generate(w: Workload, seed: int | None = None) -> dict:
 
 def random_case(seed: int, n_head: int, n_tok: int, n_kv: int, hd: int,
                 q_dtype: str = "f32", mask_kind: str = "random", sigma: float = 1.0,
-                neg_inf_frac: float = 0.2, n_inst: int = 1) -> dict:
+                neg_inf_frac: float = 0.2, n_inst: int = 1, n_kv_head: int = 1) -> dict:
     """Small random cases for parity sweeps (ragged shapes, random masks).
 
     mask_kind: "none" (no mask), "zero", "random" (each entry -inf with
     probability neg_inf_frac, else a finite value in [-2, 2] rounded to f16),
     or "full_row" (random, with token 0's row entirely -inf).
+    k and v are [n_inst, n_kv, hd], or [n_inst, n_kv_head, n_kv, hd] when
+    n_kv_head > 1.
     """
     rng = np.random.default_rng(seed)
     q = (rng.standard_normal((n_inst, n_tok, n_head, hd)) * sigma).astype(np.float32)
     if q_dtype == "f16":
         q = f16_bits(q)
-    k = f16_bits(rng.standard_normal((n_inst, n_kv, hd)) * sigma)
-    v = f16_bits(rng.standard_normal((n_inst, n_kv, hd)) * sigma)
+    kv_shape = (n_inst, n_kv, hd) if n_kv_head == 1 else (n_inst, n_kv_head, n_kv, hd)
+    k = f16_bits(rng.standard_normal(kv_shape) * sigma)
+    v = f16_bits(rng.standard_normal(kv_shape) * sigma)
     mask = None
     if mask_kind == "zero":
         mask = np.zeros((n_inst, n_tok, n_kv), dtype=np.uint16)

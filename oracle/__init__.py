@@ -65,6 +65,11 @@ def _load():
             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int]
+        lib.oracle_decode_attn_gqa_f64.restype = ctypes.c_int
+        lib.oracle_decode_attn_gqa_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -97,12 +102,13 @@ def max_threads() -> int:
 
 def decode_attn(q, k, v, mask, n_head: int, n_tok: int, n_kv: int, hd: int,
                 scale: float, q_kind: int = Q_F32, threads: int = 0,
-                return_threads: bool = False):
+                return_threads: bool = False, n_kv_head: int = 1):
     """One instance of decode attention in fp64.
 
     q    : [n_tok, n_head, hd] float32 (Q_F32, Q_F32_ROUND_F16) or uint16 f16 bits (Q_F16)
-    k, v : [n_kv, hd] uint16 f16 bits
-    mask : [n_tok, n_kv] uint16 f16 bits, or None (all zero)
+    k, v : [n_kv, hd] uint16 f16 bits; with n_kv_head > 1, [n_kv_head, n_kv, hd]
+           (query head h uses KV head h // (n_head // n_kv_head))
+    mask : [n_tok, n_kv] uint16 f16 bits, or None (all zero); shared by all heads
     returns [n_tok, n_head, hd] float64  (== ggml's [hd, n_head, n_tok])
     """
     lib = _load()
@@ -110,7 +116,8 @@ def decode_attn(q, k, v, mask, n_head: int, n_tok: int, n_kv: int, hd: int,
     qa = np.ascontiguousarray(q, dtype=qdt)
     ka = np.ascontiguousarray(k, dtype=np.uint16)
     va = np.ascontiguousarray(v, dtype=np.uint16)
-    if qa.size != n_tok * n_head * hd or ka.size != n_kv * hd or va.size != n_kv * hd:
+    kv_size = n_kv_head * n_kv * hd
+    if qa.size != n_tok * n_head * hd or ka.size != kv_size or va.size != kv_size:
         raise ValueError("oracle: tensor sizes do not match the shape arguments")
     ma = None
     if mask is not None:
@@ -118,10 +125,11 @@ def decode_attn(q, k, v, mask, n_head: int, n_tok: int, n_kv: int, hd: int,
         if ma.size != n_tok * n_kv:
             raise ValueError("oracle: mask size does not match [n_tok, n_kv]")
     out = np.empty((n_tok, n_head, hd), dtype=np.float64)
-    used = lib.oracle_decode_attn_f64(
+    used = lib.oracle_decode_attn_gqa_f64(
         qa.ctypes.data, int(q_kind), ka.ctypes.data, va.ctypes.data,
         None if ma is None else ma.ctypes.data, out.ctypes.data,
-        int(n_head), int(n_tok), int(n_kv), int(hd), float(scale), int(threads))
+        int(n_head), int(n_kv_head), int(n_tok), int(n_kv), int(hd), float(scale),
+        int(threads))
     if used < 0:
         raise RuntimeError("oracle_decode_attn_f64 failed")
     return (out, used) if return_threads else out

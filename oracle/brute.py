@@ -27,10 +27,11 @@ def float_to_half_bits(x: float) -> int:
     return struct.unpack("<H", struct.pack("<e", x))[0]
 
 
-def decode_attn(q, k, v, mask, n_head, n_tok, n_kv, hd, scale, q_is_f16=False):
+def decode_attn(q, k, v, mask, n_head, n_tok, n_kv, hd, scale, q_is_f16=False, n_kv_head=1):
     """q: flat list (len n_tok*n_head*hd) of floats, or of f16 bits if q_is_f16;
-    k, v: flat lists of f16 bits (n_kv*hd); mask: flat list of f16 bits
-    (n_tok*n_kv) or None.  Returns a flat list in [n_tok][n_head][hd] order."""
+    k, v: flat lists of f16 bits (n_kv_head*n_kv*hd; query head h reads KV head
+    h // (n_head // n_kv_head)); mask: flat list of f16 bits (n_tok*n_kv) or
+    None.  Returns a flat list in [n_tok][n_head][hd] order."""
     qf = [half_bits_to_float(x) for x in q] if q_is_f16 else [float(x) for x in q]
     kf = [half_bits_to_float(x) for x in k]
     vf = [half_bits_to_float(x) for x in v]
@@ -39,19 +40,20 @@ def decode_attn(q, k, v, mask, n_head, n_tok, n_kv, hd, scale, q_is_f16=False):
         for h in range(n_head):
             r = t * n_head + h
             qr = qf[r * hd:(r + 1) * hd]
+            kv0 = (h // (n_head // n_kv_head)) * n_kv * hd   # this head's K/V rows
             weights = []
             for j in range(n_kv):
                 mj = 0.0 if mask is None else half_bits_to_float(mask[t * n_kv + j])
                 if mj == -math.inf:
                     weights.append(0.0)
                     continue
-                dot = math.fsum(qr[e] * kf[j * hd + e] for e in range(hd))
+                dot = math.fsum(qr[e] * kf[kv0 + j * hd + e] for e in range(hd))
                 weights.append(math.exp(scale * dot + mj))
             total = math.fsum(weights)
             for d in range(hd):
                 if total == 0.0:
                     out.append(0.0)
                 else:
-                    out.append(math.fsum(weights[j] * vf[j * hd + d]
+                    out.append(math.fsum(weights[j] * vf[kv0 + j * hd + d]
                                          for j in range(n_kv)) / total)
     return out

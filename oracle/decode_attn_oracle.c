@@ -113,19 +113,26 @@ int oracle_max_threads(void)
 }
 
 /*
- * One attention instance.
- *   q    : [n_tok][n_head][hd]  f32 (q_kind 0/2) or f16 bits (q_kind 1)
- *   k, v : [n_kv][hd]           f16 bits
- *   mask : [n_tok][n_kv]        f16 bits, additive; NULL = all zero
- *   out  : [n_tok][n_head][hd]  fp64
+ * One attention instance with n_kv_head KV heads (grouped-query attention).
+ *   q    : [n_tok][n_head][hd]       f32 (q_kind 0/2) or f16 bits (q_kind 1)
+ *   k, v : [n_kv_head][n_kv][hd]     f16 bits
+ *   mask : [n_tok][n_kv]             f16 bits, additive, shared by all heads;
+ *                                    NULL = all zero
+ *   out  : [n_tok][n_head][hd]       fp64
+ * Query head h attends over KV head h / (n_head / n_kv_head): consecutive
+ * query heads form a group sharing one KV head (the flash-attention node's
+ * broadcast of KV heads over query heads).  n_kv_head = 1 is the pages' case,
+ * one KV head shared by every query head.
  * Returns the number of threads used, or -1 on bad arguments / no memory.
  */
-int oracle_decode_attn_f64(const void *q, int q_kind,
-                           const uint16_t *k, const uint16_t *v, const uint16_t *mask,
-                           double *out, int n_head, int n_tok, int n_kv, int hd,
-                           double scale, int n_threads)
+int oracle_decode_attn_gqa_f64(const void *q, int q_kind,
+                               const uint16_t *k, const uint16_t *v, const uint16_t *mask,
+                               double *out, int n_head, int n_kv_head, int n_tok, int n_kv,
+                               int hd, double scale, int n_threads)
 {
     if (!q || !k || !v || !out || n_head < 1 || n_tok < 1 || n_kv < 1 || hd < 1)
+        return -1;
+    if (n_kv_head < 1 || n_head % n_kv_head != 0)
         return -1;
     if (q_kind < ORACLE_Q_F32 || q_kind > ORACLE_Q_F32_ROUND_F16)
         return -1;
@@ -135,7 +142,8 @@ int oracle_decode_attn_f64(const void *q, int q_kind,
 #else
     (void)n_threads;
 #endif
-    const size_t kv_elems = (size_t)n_kv * (size_t)hd;
+    const int group = n_head / n_kv_head; /* query heads per KV head */
+    const size_t kv_elems = (size_t)n_kv_head * (size_t)n_kv * (size_t)hd;
     double *K = (double *)malloc(kv_elems * sizeof(double));
     double *V = (double *)malloc(kv_elems * sizeof(double));
     if (!K || !V) {
@@ -172,12 +180,16 @@ int oracle_decode_attn_f64(const void *q, int q_kind,
                 continue;
             }
             const int t = r / n_head; /* row r = t*n_head + h (t-major) */
+            const int h = r % n_head;
+            /* this row's KV head */
+            const double *Kh = K + (size_t)(h / group) * (size_t)n_kv * (size_t)hd;
+            const double *Vh = V + (size_t)(h / group) * (size_t)n_kv * (size_t)hd;
             for (int e = 0; e < hd; ++e)
                 qr[e] = q_at(q, q_kind, (size_t)r * hd + e);
             /* logits: scale * <q, K_j> + mask[t][j] */
             double m = -INFINITY;
             for (int j = 0; j < n_kv; ++j) {
-                const double *kj = K + (size_t)j * hd;
+                const double *kj = Kh + (size_t)j * hd;
                 double dot = 0.0;
                 for (int e = 0; e < hd; ++e)
                     dot += qr[e] * kj[e];
@@ -202,7 +214,7 @@ int oracle_decode_attn_f64(const void *q, int q_kind,
                         continue; /* exactly zero weight */
                     const double p = exp(s[j] - m);
                     l += p;
-                    const double *vj = V + (size_t)j * hd;
+                    const double *vj = Vh + (size_t)j * hd;
                     for (int d = 0; d < hd; ++d)
                         acc[d] += p * vj[d];
                 }
@@ -217,4 +229,14 @@ int oracle_decode_attn_f64(const void *q, int q_kind,
     free(K);
     free(V);
     return failed ? -1 : used;
+}
+
+/* The pages' case: one KV head shared by every query head. */
+int oracle_decode_attn_f64(const void *q, int q_kind,
+                           const uint16_t *k, const uint16_t *v, const uint16_t *mask,
+                           double *out, int n_head, int n_tok, int n_kv, int hd,
+                           double scale, int n_threads)
+{
+    return oracle_decode_attn_gqa_f64(q, q_kind, k, v, mask, out, n_head, 1, n_tok, n_kv, hd,
+                                      scale, n_threads);
 }

@@ -102,6 +102,63 @@ def test_oracle_matches_brute_force(oracle_mod, seed):
     assert np.max(np.abs(got - want)) <= tol
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_gqa_oracle_matches_brute_force(oracle_mod, seed):
+    """Several KV heads: query head h reads KV head h // (n_head // n_kv_head)."""
+    rng = np.random.default_rng(3000 + seed)
+    n_kv_head, group = int(rng.integers(2, 4)), int(rng.integers(1, 3))
+    n_head, n_tok = n_kv_head * group, int(rng.integers(1, 4))
+    n_kv, hd = int(rng.integers(1, 6)), int(rng.integers(1, 7))
+    q_kind = [oracle_mod.Q_F32, oracle_mod.Q_F16][seed % 2]
+    c = random_case(seed, n_head, n_tok, n_kv, hd,
+                    q_dtype="f16" if q_kind == oracle_mod.Q_F16 else "f32",
+                    mask_kind=["random", "none", "full_row"][seed % 3], sigma=0.7,
+                    neg_inf_frac=0.3, n_kv_head=n_kv_head)
+    scale = float(np.float32(1.0 / math.sqrt(hd)))
+    m = None if c["mask"] is None else c["mask"][0]
+    got = oracle_mod.decode_attn(c["q"][0], c["k"][0], c["v"][0], m, n_head, n_tok, n_kv, hd,
+                                 scale, q_kind=q_kind, n_kv_head=n_kv_head).reshape(-1)
+    want = np.array(brute.decode_attn(c["q"][0].reshape(-1).tolist(),
+                                      c["k"][0].reshape(-1).tolist(),
+                                      c["v"][0].reshape(-1).tolist(),
+                                      None if m is None else m.reshape(-1).tolist(),
+                                      n_head, n_tok, n_kv, hd, scale,
+                                      q_is_f16=(q_kind == oracle_mod.Q_F16),
+                                      n_kv_head=n_kv_head))
+    tol = 1e-12 * max(1.0, float(np.max(np.abs(want))))
+    assert np.max(np.abs(got - want)) <= tol
+
+
+def test_gqa_single_key_selects_each_groups_value_row(oracle_mod):
+    """With one key, head h's output is row 0 of KV head h // G exactly: pins
+    the head-to-group mapping (a transposed or off-by-one mapping picks the
+    wrong row)."""
+    n_head, n_kvh, n_tok, hd = 12, 4, 3, 8
+    c = random_case(41, n_head, n_tok, 1, hd, mask_kind="none", n_kv_head=n_kvh)
+    out = oracle_mod.decode_attn(c["q"][0], c["k"][0], c["v"][0], None, n_head, n_tok, 1, hd,
+                                 0.3, n_kv_head=n_kvh)
+    vals = c["v"][0][:, 0, :].view(np.float16).astype(np.float64)     # [n_kvh, hd]
+    for h in range(n_head):
+        assert np.array_equal(out[:, h, :], np.broadcast_to(vals[h // (n_head // n_kvh)],
+                                                             (n_tok, hd)))
+
+
+def test_gqa_identical_keys_give_each_groups_mean(oracle_mod):
+    """Identical keys inside each KV head: every head of a group outputs the
+    mean of that group's value rows (the softmax is uniform)."""
+    n_head, n_kvh, n_tok, n_kv, hd = 6, 3, 2, 7, 4
+    c = random_case(43, n_head, n_tok, n_kv, hd, mask_kind="none", n_kv_head=n_kvh)
+    k = c["k"][0].copy()
+    k[:, :, :] = k[:, :1, :]
+    out = oracle_mod.decode_attn(c["q"][0], k, c["v"][0], None, n_head, n_tok, n_kv, hd, 0.5,
+                                 n_kv_head=n_kvh)
+    v = c["v"][0].view(np.float16).astype(np.float64)
+    for h in range(n_head):
+        want = np.array([math.fsum(v[h // 2, :, d]) / n_kv for d in range(hd)])
+        np.testing.assert_allclose(out[:, h, :], np.broadcast_to(want, (n_tok, hd)),
+                                   rtol=1e-14, atol=1e-15)
+
+
 def test_hand_worked_cases(oracle_mod):
     with open(os.path.join(HERE, "golden", "hand_cases.json")) as f:
         cases = json.load(f)["cases"]
@@ -277,6 +334,27 @@ def test_q16_and_rounded_f32_query_agree(oracle_mod):
 
 
 # --------------------------------------------------------------------------- library cross-check
+
+def test_gqa_matches_torch_sdpa_float64(oracle_mod):
+    torch = pytest.importorskip("torch")
+    n_head, n_kvh, n_tok, n_kv, hd = 8, 2, 5, 131, 32
+    c = random_case(77, n_head, n_tok, n_kv, hd, mask_kind="random", neg_inf_frac=0.1,
+                    n_kv_head=n_kvh)
+    scale = 0.2
+    out = oracle_mod.decode_attn(c["q"][0], c["k"][0], c["v"][0], c["mask"][0], n_head, n_tok,
+                                 n_kv, hd, scale, n_kv_head=n_kvh)
+    q = torch.from_numpy(c["q"][0].astype(np.float64)).permute(1, 0, 2)       # [h, t, d]
+    k = torch.from_numpy(c["k"][0].view(np.float16).astype(np.float64))      # [kvh, kv, d]
+    v = torch.from_numpy(c["v"][0].view(np.float16).astype(np.float64))
+    k = k.repeat_interleave(n_head // n_kvh, dim=0)                          # heads of a group
+    v = v.repeat_interleave(n_head // n_kvh, dim=0)
+    m = torch.from_numpy(c["mask"][0].view(np.float16).astype(np.float64))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0), attn_mask=m, scale=scale)[0]
+    ref = ref.permute(1, 0, 2).numpy()
+    finite = np.isfinite(ref).all(axis=(1, 2))
+    np.testing.assert_allclose(out[finite], ref[finite], rtol=1e-12, atol=1e-13)
+
 
 @pytest.mark.parametrize("seed", range(4))
 def test_matches_torch_sdpa_float64(oracle_mod, seed):
