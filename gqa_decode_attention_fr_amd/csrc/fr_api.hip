@@ -149,11 +149,18 @@ int check_flags(int q_format, unsigned flags) {
 
 int validate(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
              const uint16_t *mask, const float *out, int n_inst, int64_t q_stride,
-             int64_t kv_stride, int64_t mask_stride, int64_t out_stride, int n_head, int n_tok,
-             int n_kv, int hd, float scale, unsigned flags) {
+             int64_t kv_stride, int64_t mask_stride, int64_t out_stride, int n_head,
+             int n_kvh, int64_t kvh_stride, int n_tok, int n_kv, int hd, float scale,
+             unsigned flags) {
   if (!q || !k || !v || !out) return FR_ERR_INVALID;
   int st = check_sizes(n_inst, n_head, n_tok, n_kv, hd);
   if (st != FR_OK) return st;
+  // KV heads: a divisor of n_head, each a 16-byte aligned [n_kv][hd] block
+  if (n_kvh < 1 || n_head % n_kvh != 0) return FR_ERR_INVALID;
+  if (n_kvh > 1 && (kvh_stride < (int64_t)n_kv * hd || (kvh_stride * 2) % 16))
+    return FR_ERR_INVALID;
+  const int64_t kv_elems = (int64_t)(n_kvh - 1) * (n_kvh > 1 ? kvh_stride : 0) +
+                           (int64_t)n_kv * hd;   // one instance's K (or V)
   st = check_flags(q_format, flags);
   if (st != FR_OK) return st;
   if (!std::isfinite(scale)) return FR_ERR_INVALID;
@@ -165,7 +172,7 @@ int validate(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
   if (n_inst > 1) {
     if (q_stride < 0 || (q_stride != 0 && q_stride < M * hd)) return FR_ERR_INVALID;
     if ((q_stride * (int64_t)qsize) % 16) return FR_ERR_INVALID;
-    if (kv_stride < 0 || (kv_stride != 0 && kv_stride < (int64_t)n_kv * hd)) return FR_ERR_INVALID;
+    if (kv_stride < 0 || (kv_stride != 0 && kv_stride < kv_elems)) return FR_ERR_INVALID;
     if ((kv_stride * 2) % 16) return FR_ERR_INVALID;
     if (mask_stride < 0 || (mask_stride != 0 && mask_stride < (int64_t)n_tok * n_kv))
       return FR_ERR_INVALID;
@@ -175,8 +182,8 @@ int validate(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
   }
   const Range ro = span(out, n_inst, out_stride, M * hd, 4);
   if (overlaps(ro, span(q, n_inst, q_stride, M * hd, qsize))) return FR_ERR_INVALID;
-  if (overlaps(ro, span(k, n_inst, kv_stride, (int64_t)n_kv * hd, 2))) return FR_ERR_INVALID;
-  if (overlaps(ro, span(v, n_inst, kv_stride, (int64_t)n_kv * hd, 2))) return FR_ERR_INVALID;
+  if (overlaps(ro, span(k, n_inst, kv_stride, kv_elems, 2))) return FR_ERR_INVALID;
+  if (overlaps(ro, span(v, n_inst, kv_stride, kv_elems, 2))) return FR_ERR_INVALID;
   if (mask && overlaps(ro, span(mask, n_inst, mask_stride, (int64_t)n_tok * n_kv, 2)))
     return FR_ERR_INVALID;
   return FR_OK;
@@ -232,15 +239,17 @@ int library_ws(size_t need, hipStream_t stream, bool check_capture, void **out) 
 
 int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const uint16_t *mask,
         float *out, int n_inst, int64_t q_stride, int64_t kv_stride, int64_t mask_stride,
-        int64_t out_stride, int n_head, int n_tok, int n_kv, int hd, float scale,
-        unsigned flags, void *workspace, size_t workspace_bytes, bool caller_ws,
-        void *stream) {
+        int64_t out_stride, int n_head, int n_kvh, int64_t kvh_stride, int n_tok, int n_kv,
+        int hd, float scale, unsigned flags, void *workspace, size_t workspace_bytes,
+        bool caller_ws, void *stream) {
   int st = validate(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride,
-                    out_stride, n_head, n_tok, n_kv, hd, scale, flags);
+                    out_stride, n_head, n_kvh, kvh_stride, n_tok, n_kv, hd, scale, flags);
   if (st != FR_OK) return st;
   if (n_inst == 1) q_stride = kv_stride = mask_stride = out_stride = 0;
+  if (n_kvh == 1) kvh_stride = 0;
+  // the kernels run on units (instance, KV head) of n_head / n_kvh query heads
   Plan plan;
-  st = fr::make_plan(n_inst, n_head, n_tok, n_kv, hd, flags, &plan);
+  st = fr::make_plan(n_inst * n_kvh, n_head / n_kvh, n_tok, n_kv, hd, flags, &plan);
   if (st != FR_OK) return st;
   if (caller_ws) {
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
@@ -265,13 +274,15 @@ int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const
   p.n_tok = n_tok;
   p.n_kv = n_kv;
   p.hd = hd;
+  p.n_kvh = n_kvh;
+  p.kvh_stride = kvh_stride;
   p.scale = scale;
   p.qmode = q_format == FR_Q_F16 ? fr::kQF16 : ((flags & FR_Q_ROUND_F16) ? fr::kQRound : fr::kQHiLo);
   if (fr::debug_on())
     std::fprintf(stderr,
-                 "[fr_decode_attn] variant=%d n_inst=%d M=%d n_kv=%d hd=%d qmode=%d splits=%d "
-                 "chunk=%d waves=%d tiles=%d rowblk=%d grid=%d ws=%zu\n",
-                 plan.variant, n_inst, n_head * n_tok, n_kv, hd, p.qmode, plan.n_split,
+                 "[fr_decode_attn] variant=%d n_inst=%d kv_heads=%d M=%d n_kv=%d hd=%d qmode=%d "
+                 "splits=%d chunk=%d waves=%d tiles=%d rowblk=%d grid=%d ws=%zu\n",
+                 plan.variant, n_inst, n_kvh, n_head * n_tok, n_kv, hd, p.qmode, plan.n_split,
                  plan.chunk, plan.waves, plan.tiles, plan.n_rowblk, plan.grid, plan.ws_bytes);
   hipError_t err = plan.variant == fr::kDecomposed
                        ? fr::launch_decomposed(p, plan, workspace, (hipStream_t)stream)
@@ -286,15 +297,15 @@ extern "C" {
 int fr_decode_attn(const float *q, const uint16_t *k, const uint16_t *v, const uint16_t *mask,
                    float *out, int n_head, int n_tok, int n_kv, int hd, float scale,
                    void *stream) {
-  return run(q, FR_Q_F32, k, v, mask, out, 1, 0, 0, 0, 0, n_head, n_tok, n_kv, hd, scale, 0u,
-             nullptr, 0, false, stream);
+  return run(q, FR_Q_F32, k, v, mask, out, 1, 0, 0, 0, 0, n_head, 1, 0, n_tok, n_kv, hd, scale,
+             0u, nullptr, 0, false, stream);
 }
 
 int fr_decode_attn_q16(const uint16_t *q16, const uint16_t *k, const uint16_t *v,
                        const uint16_t *mask, float *out, int n_head, int n_tok, int n_kv, int hd,
                        float scale, void *stream) {
-  return run(q16, FR_Q_F16, k, v, mask, out, 1, 0, 0, 0, 0, n_head, n_tok, n_kv, hd, scale, 0u,
-             nullptr, 0, false, stream);
+  return run(q16, FR_Q_F16, k, v, mask, out, 1, 0, 0, 0, 0, n_head, 1, 0, n_tok, n_kv, hd,
+             scale, 0u, nullptr, 0, false, stream);
 }
 
 int fr_decode_attn_batched(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
@@ -302,7 +313,7 @@ int fr_decode_attn_batched(const void *q, int q_format, const uint16_t *k, const
                            int64_t kv_stride, int64_t mask_stride, int64_t out_stride,
                            int n_head, int n_tok, int n_kv, int hd, float scale, void *stream) {
   return run(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride, out_stride,
-             n_head, n_tok, n_kv, hd, scale, 0u, nullptr, 0, false, stream);
+             n_head, 1, 0, n_tok, n_kv, hd, scale, 0u, nullptr, 0, false, stream);
 }
 
 int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
@@ -311,8 +322,19 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k, const uint
                       int n_tok, int n_kv, int hd, float scale, unsigned flags, void *workspace,
                       size_t workspace_bytes, void *stream) {
   return run(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride, out_stride,
-             n_head, n_tok, n_kv, hd, scale, flags, workspace, workspace_bytes,
+             n_head, 1, 0, n_tok, n_kv, hd, scale, flags, workspace, workspace_bytes,
              workspace != nullptr, stream);
+}
+
+int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *mask, float *out, int n_inst, int64_t q_stride,
+                       int64_t kv_stride, int64_t mask_stride, int64_t out_stride, int n_head,
+                       int n_kv_head, int64_t kv_head_stride, int n_tok, int n_kv, int hd,
+                       float scale, unsigned flags, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  return run(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride, out_stride,
+             n_head, n_kv_head, kv_head_stride, n_tok, n_kv, hd, scale, flags, workspace,
+             workspace_bytes, workspace != nullptr, stream);
 }
 
 size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv, int hd,

@@ -14,7 +14,9 @@
 //   (sum_kernel     adds the key-split partials of pv_kernel when it is split)
 //
 // It exists for A/B comparison with the fused split-KV kernel: the S and P
-// round trips are exactly the HBM traffic that fusion removes.
+// round trips are exactly the HBM traffic that fusion removes.  Like the fused
+// path it works on units (instance, KV head); S, P and the partials are
+// indexed by unit and unit row, the inputs and the output by instance and row.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -33,8 +35,9 @@ struct QkArgs {
   const void *q;
   const uint16_t *k;
   float *s;
-  int64_t q_stride, kv_stride;
+  int64_t q_stride, kv_stride, kvh_stride;
   int M, n_kv, kv_pad, n_rowblk, n_kblk;
+  int n_kvh, grp, n_head;
   float scale;
 };
 
@@ -51,9 +54,10 @@ __global__ __launch_bounds__(kThreads) void qk_kernel(QkArgs a) {
   const int kblk = bid % a.n_kblk;
   bid /= a.n_kblk;
   const int rowblk = bid % a.n_rowblk;
-  const int inst = bid / a.n_rowblk;
+  const int inst = bid / a.n_rowblk;   // unit
+  const int kvh = inst % a.n_kvh, rinst = inst / a.n_kvh;
   const int kb0 = kblk * KB;
-  const uint16_t *kbase = a.k + (int64_t)inst * a.kv_stride;
+  const uint16_t *kbase = a.k + (int64_t)rinst * a.kv_stride + (int64_t)kvh * a.kvh_stride;
 
   for (int u = tid; u < KB * GPR; u += kThreads) {
     const int row = u / GPR, c = u % GPR;
@@ -66,15 +70,16 @@ __global__ __launch_bounds__(kThreads) void qk_kernel(QkArgs a) {
   const int tile0 = rowblk * (kWaves * TILES) + wave * TILES;
   if (tile0 * 16 >= a.M) return;
   const void *qinst = (QMODE == kQF16)
-                          ? (const void *)((const uint16_t *)a.q + (int64_t)inst * a.q_stride)
-                          : (const void *)((const float *)a.q + (int64_t)inst * a.q_stride);
+                          ? (const void *)((const uint16_t *)a.q + (int64_t)rinst * a.q_stride)
+                          : (const void *)((const float *)a.q + (int64_t)rinst * a.q_stride);
   half8 qh[TILES][KS], ql[TILES][KS];
 #pragma unroll
   for (int i = 0; i < TILES; ++i) {
     const int r = (tile0 + i) * 16 + l16;
+    const int64_t qrow = r < a.M ? (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      load_q8<QMODE>(qinst, (int64_t)r * HD + ks * 32 + g * 8, r < a.M, qh[i][ks], ql[i][ks]);
+      load_q8<QMODE>(qinst, qrow + ks * 32 + g * 8, r < a.M, qh[i][ks], ql[i][ks]);
   }
   float4v s[TILES][4];
 #pragma unroll
@@ -113,7 +118,7 @@ struct SoftmaxArgs {
   const uint16_t *mask;
   uint16_t *p;
   int64_t mask_stride;
-  int M, n_head, n_tok, n_kv, kv_pad, rows;
+  int M, grp, n_kvh, n_tok, n_kv, kv_pad, rows;   // rows = units * M
 };
 
 // One wavefront per query row: online (max, sum) per lane over the row, then
@@ -122,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(SoftmaxArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= a.rows) return;
-  const int inst = row / a.M, r = row % a.M, t = r / a.n_head;
+  // unit row r of unit u = row / M is token r / grp of instance u / n_kvh
+  const int inst = row / a.M / a.n_kvh, r = row % a.M, t = r / a.grp;
   const float *srow = a.s + (int64_t)row * a.kv_pad;
   const uint16_t *mrow =
       a.mask ? a.mask + (int64_t)inst * a.mask_stride + (int64_t)t * a.n_kv : nullptr;
@@ -165,8 +171,9 @@ struct PvArgs {
   const uint16_t *v;
   float *out;
   float *part;
-  int64_t kv_stride, out_stride;
+  int64_t kv_stride, kvh_stride, out_stride;
   int M, n_kv, kv_pad, n_rowblk, n_split, chunk;
+  int n_kvh, grp, n_head;
 };
 
 template <int HD, int TILES>
@@ -182,8 +189,9 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(PvArgs a) {
   const int split = bid % a.n_split;
   bid /= a.n_split;
   const int rowblk = bid % a.n_rowblk;
-  const int inst = bid / a.n_rowblk;
-  const uint16_t *vbase = a.v + (int64_t)inst * a.kv_stride;
+  const int inst = bid / a.n_rowblk;   // unit
+  const int kvh = inst % a.n_kvh, rinst = inst / a.n_kvh;
+  const uint16_t *vbase = a.v + (int64_t)rinst * a.kv_stride + (int64_t)kvh * a.kvh_stride;
   const int key_begin = split * a.chunk;
   const int key_end = min(key_begin + a.chunk, a.n_kv);
   const int tile0 = rowblk * (kWaves * TILES) + wave * TILES;
@@ -246,7 +254,8 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(PvArgs a) {
     const int r = (tile0 + i) * 16 + l16;
     if (r >= a.M) continue;
     float *dst = (a.n_split == 1)
-                     ? a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD
+                     ? a.out + (int64_t)rinst * a.out_stride +
+                           (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD
                      : a.part + (((int64_t)inst * a.n_split + split) * a.M + r) * HD;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *(float4v *)(dst + dt * 16 + 4 * g) = o[i][dt];
@@ -257,7 +266,8 @@ struct SumArgs {
   const float *part;
   float *out;
   int64_t out_stride;
-  int M, hd, n_split, n_inst;
+  int M, hd, n_split, n_inst;   // n_inst counts units
+  int n_kvh, grp, n_head;
 };
 
 // out = sum over key splits of the PV partials, in split order.
@@ -272,7 +282,9 @@ __global__ __launch_bounds__(256) void sum_kernel(SumArgs a) {
   for (int s = 0; s < a.n_split; ++s)
     acc += *(const float4v *)(a.part + (((int64_t)inst * a.n_split + s) * a.M + r) * a.hd +
                               4 * d4);
-  *(float4v *)(a.out + (int64_t)inst * a.out_stride + (int64_t)r * a.hd + 4 * d4) = acc;
+  const int64_t orow = (int64_t)(inst / a.n_kvh) * a.out_stride +
+                       (int64_t)instance_row(r, inst % a.n_kvh, a.grp, a.n_head) * a.hd;
+  *(float4v *)(a.out + orow + 4 * d4) = acc;
 }
 
 template <int HD>
@@ -295,7 +307,8 @@ void launch_pv(dim3 grid, hipStream_t st, const PvArgs &a) {
 
 hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace,
                              hipStream_t stream) {
-  const int M = p.n_head * p.n_tok;
+  const int M = p.unit_rows();
+  const int U = p.units();
   const int n_kblk = (p.n_kv + KB - 1) / KB;
   const int kv_pad = n_kblk * KB;
   char *ws = (char *)workspace;
@@ -306,9 +319,9 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
     return ptr;
   };
   float *part = nullptr;
-  if (plan.n_split > 1) part = (float *)take((size_t)p.n_inst * plan.n_split * M * p.hd * 4);
-  float *s = (float *)take((size_t)p.n_inst * M * kv_pad * 4);
-  uint16_t *pm = (uint16_t *)take((size_t)p.n_inst * M * kv_pad * 2);
+  if (plan.n_split > 1) part = (float *)take((size_t)U * plan.n_split * M * p.hd * 4);
+  float *s = (float *)take((size_t)U * M * kv_pad * 4);
+  uint16_t *pm = (uint16_t *)take((size_t)U * M * kv_pad * 2);
   if (off > plan.ws_bytes) return hipErrorInvalidValue;
 
   QkArgs qa;
@@ -317,6 +330,10 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   qa.s = s;
   qa.q_stride = p.q_stride;
   qa.kv_stride = p.kv_stride;
+  qa.kvh_stride = p.kvh_stride;
+  qa.n_kvh = p.n_kvh;
+  qa.grp = p.grp();
+  qa.n_head = p.n_head;
   qa.M = M;
   qa.n_kv = p.n_kv;
   qa.kv_pad = kv_pad;
@@ -326,7 +343,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   hipEvent_t ev0, ev1;
   profile_events(&ev0, &ev1);
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
-  const dim3 qgrid(p.n_inst * plan.n_rowblk * n_kblk);
+  const dim3 qgrid(U * plan.n_rowblk * n_kblk);
   switch (p.hd) {
     case 64: launch_qk<64>(p.qmode, qgrid, stream, qa); break;
     case 128: launch_qk<128>(p.qmode, qgrid, stream, qa); break;
@@ -341,11 +358,12 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   sa.p = pm;
   sa.mask_stride = p.mask_stride;
   sa.M = M;
-  sa.n_head = p.n_head;
+  sa.grp = p.grp();
+  sa.n_kvh = p.n_kvh;
   sa.n_tok = p.n_tok;
   sa.n_kv = p.n_kv;
   sa.kv_pad = kv_pad;
-  sa.rows = p.n_inst * M;
+  sa.rows = U * M;
   hipLaunchKernelGGL(softmax_kernel, dim3((sa.rows + kWaves - 1) / kWaves), dim3(kThreads), 0,
                      stream, sa);
   err = hipGetLastError();
@@ -357,14 +375,18 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   pa.out = p.out;
   pa.part = part;
   pa.kv_stride = p.kv_stride;
+  pa.kvh_stride = p.kvh_stride;
   pa.out_stride = p.out_stride;
+  pa.n_kvh = p.n_kvh;
+  pa.grp = p.grp();
+  pa.n_head = p.n_head;
   pa.M = M;
   pa.n_kv = p.n_kv;
   pa.kv_pad = kv_pad;
   pa.n_rowblk = plan.n_rowblk;
   pa.n_split = plan.n_split;
   pa.chunk = plan.chunk;
-  const dim3 pgrid(p.n_inst * plan.n_rowblk * plan.n_split);
+  const dim3 pgrid(U * plan.n_rowblk * plan.n_split);
   switch (p.hd) {
     case 64: launch_pv<64>(pgrid, stream, pa); break;
     case 128: launch_pv<128>(pgrid, stream, pa); break;
@@ -381,8 +403,11 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   ua.M = M;
   ua.hd = p.hd;
   ua.n_split = plan.n_split;
-  ua.n_inst = p.n_inst;
-  const int64_t threads = (int64_t)p.n_inst * M * (p.hd / 4);
+  ua.n_inst = U;
+  ua.n_kvh = p.n_kvh;
+  ua.grp = p.grp();
+  ua.n_head = p.n_head;
+  const int64_t threads = (int64_t)U * M * (p.hd / 4);
   hipLaunchKernelGGL(sum_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                      ua);
   err = hipGetLastError();

@@ -23,6 +23,14 @@ static __device__ __forceinline__ float4v mfma16x16x32(half8 a, half8 b, float4v
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Row of the instance that unit row rho of KV head kv stands for (see the
+// KV-head groups of Problem): rho = t*grp + j  ->  t*n_head + kv*grp + j.
+static __device__ __forceinline__ int instance_row(int rho, int kv, int grp, int n_head) {
+  if (grp == n_head) return rho;   // one KV head
+  const int t = rho / grp;
+  return t * n_head + kv * grp + (rho - t * grp);
+}
+
 static __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 static __device__ __forceinline__ _Float16 bits_to_half(uint16_t b) {

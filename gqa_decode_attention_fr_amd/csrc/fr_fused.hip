@@ -60,10 +60,12 @@ struct SplitArgs {
   const uint16_t *v;
   const uint16_t *mask;
   float *out;
-  float *part_o;    // [n_inst][n_split][M][hd] unnormalised partial outputs
-  float2v *part_ml; // [n_inst][n_split][M] (running max in log2 units, sum)
+  float *part_o;    // [units][n_split][M][hd] unnormalised partial outputs
+  float2v *part_ml; // [units][n_split][M] (running max in log2 units, sum)
   int64_t q_stride, kv_stride, mask_stride, out_stride;
-  int n_head, n_tok, n_kv, M;
+  int64_t kvh_stride; // elements between the KV heads of one instance
+  int n_head, n_tok, n_kv, M;   // n_head: all query heads; M: rows of one unit
+  int n_kvh, grp;     // KV heads per instance, query heads per KV head
   int n_split, chunk, n_rowblk;
   int tpr;          // 16-row tiles per row block (<= NW * TPW)
   float scale;      // applied to q.k before the mask
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   // Workgroup -> (instance, key split, row block).  Workgroup b runs on XCD
   // b % 8, and each XCD has its own L2: the row blocks of one (instance,
   // split) pair read the same K/V chunk, so they take workgroups 8 apart (the
-  // same XCD, dispatched close together).  Pairs x = inst*n_split + split go
+  // same XCD, dispatched close together).  Pairs x = unit*n_split + split go
   // in groups of 8 (fewer in the last group): group gr holds its pairs' row
   // block 0, then row block 1, ...
   const int n_pair = gridDim.x / a.n_rowblk;
@@ -267,11 +269,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   const int rowblk = __builtin_amdgcn_readfirstlane(in_gr / gcnt);
   const int pair = 8 * gr + in_gr - rowblk * gcnt;
   const int split = __builtin_amdgcn_readfirstlane(pair % a.n_split);
+  // the unit (instance, KV head) of this workgroup; its partials are indexed
+  // by the unit, its inputs and output by the instance and the KV head
   const int inst = __builtin_amdgcn_readfirstlane(pair / a.n_split);
+  const int kvh = __builtin_amdgcn_readfirstlane(inst % a.n_kvh);
+  const int rinst = __builtin_amdgcn_readfirstlane(inst / a.n_kvh);
 
-  const uint16_t *kbase = a.k + (int64_t)inst * a.kv_stride;
-  const uint16_t *vbase = a.v + (int64_t)inst * a.kv_stride;
-  const uint16_t *mbase = a.mask ? a.mask + (int64_t)inst * a.mask_stride : nullptr;
+  const int64_t kv_off = (int64_t)rinst * a.kv_stride + (int64_t)kvh * a.kvh_stride;
+  const uint16_t *kbase = a.k + kv_off;
+  const uint16_t *vbase = a.v + kv_off;
+  const uint16_t *mbase = a.mask ? a.mask + (int64_t)rinst * a.mask_stride : nullptr;
   const int key_begin = split * a.chunk;
   const int key_end = min(key_begin + a.chunk, a.n_kv);
   const int nblk = (key_end - key_begin + KB - 1) / KB;
@@ -364,8 +371,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   float4v qraw[TPW][KS][2];
   bool q_on[TPW];
   const void *qinst = (QMODE == kQF16)
-                          ? (const void *)((const uint16_t *)a.q + (int64_t)inst * a.q_stride)
-                          : (const void *)((const float *)a.q + (int64_t)inst * a.q_stride);
+                          ? (const void *)((const uint16_t *)a.q + (int64_t)rinst * a.q_stride)
+                          : (const void *)((const float *)a.q + (int64_t)rinst * a.q_stride);
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int tile = tile_base + kWaves * i;
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     const bool in_blk = wave + kWaves * i < a.tpr;   // tile belongs to this row block
     q_on[i] = r < a.M && in_blk;
     // every lane loads (rows out of range read row 0 and are zeroed after the wait)
-    const int64_t rbase = q_on[i] ? (int64_t)r * HD : 0;
+    const int64_t rbase = q_on[i] ? (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int64_t off = rbase + ks * 32 + g * 8;
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     const int qk = l16 & (GPR - 1);
     const int vrl = 8 * g + (l16 >> 2);
     const int sv = swz_v(vrl, GPR);
-    const float inv_nh = 1.f / (float)a.n_head;
+    const float inv_nh = 1.f / (float)a.grp;
 #pragma unroll
     for (int si = 0; si < NAS; ++si) {
       Stage<HD, NW> &st = si ? st1 : st0;
@@ -492,8 +499,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       for (int j = 0; j < NVO; ++j) vaddr_s[si][j] = vb + 16 * ((2 * j + ((l16 & 3) >> 1)) ^ sv);
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
-        // token of this lane's row r = tile*16 + l16: t = r / n_head through a
-        // float reciprocal (exact: r < 2^15 and the rounding margin is 0.5/n_head)
+        // token of this lane's unit row r = tile*16 + l16: t = r / grp through a
+        // float reciprocal (exact: r < 2^15 and the rounding margin is 0.5/grp)
         const int r = (tile_base + kWaves * i) * 16 + l16;
         const int t = min((int)(((float)r + 0.5f) * inv_nh), a.n_tok - 1);
 #pragma unroll
@@ -786,7 +793,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     if (r >= a.M || wave + kWaves * i >= a.tpr) continue;
     if (a.n_split == 1) {
       const float inv = (l > 0.f) ? 1.f / l : 0.f;
-      float *orow = a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD;
+      float *orow = a.out + (int64_t)rinst * a.out_stride +
+                    (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) *(float4v *)(orow + dt * 16 + 4 * g) = o[i][dt] * inv;
     } else {
@@ -806,7 +814,8 @@ struct CombineArgs {
   const float2v *part_ml;
   float *out;
   int64_t out_stride;
-  int M, n_split, n_inst;
+  int M, n_split, n_inst;   // n_inst counts units (instance, KV head)
+  int n_kvh, grp, n_head;
 };
 
 // 256 threads = RW rows x G split groups x (HD/4) columns of 4 consecutive d,
@@ -831,7 +840,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int c = threadIdx.x % C;
   const int g = (threadIdx.x / C) % G;
   const int rw = threadIdx.x / (C * G);
-  const int row = blockIdx.x * RW + rw;          // over n_inst * M
+  const int row = blockIdx.x * RW + rw;          // over units * M
   const bool on = row < a.n_inst * a.M;
   const int r = on ? row % a.M : 0;
   const int inst = on ? row / a.M : 0;
@@ -892,7 +901,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   if (!on) return;
   const float4v out = (l > 0.f) ? acc * (1.f / l) : float4v{0.f, 0.f, 0.f, 0.f};
   // streaming store: the output is not read again by this call
-  __builtin_nontemporal_store(out, (float4v *)(a.out + (int64_t)inst * a.out_stride + (int64_t)r * HD + 4 * c));
+  const int kvh = inst % a.n_kvh;
+  const int64_t orow = (int64_t)(inst / a.n_kvh) * a.out_stride +
+                       (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD;
+  __builtin_nontemporal_store(out, (float4v *)(a.out + orow + 4 * c));
 }
 
 // Split groups of the combine: enough that each thread has at most R = 8 splits
@@ -962,7 +974,7 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   }
   if (!fn) return hipErrorInvalidValue;
 
-  const int M = p.n_head * p.n_tok;
+  const int M = p.unit_rows();
   SplitArgs a;
   a.q = p.q;
   a.k = p.k;
@@ -973,16 +985,19 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   a.kv_stride = p.kv_stride;
   a.mask_stride = p.mask_stride;
   a.out_stride = p.out_stride;
+  a.kvh_stride = p.kvh_stride;
   a.n_head = p.n_head;
   a.n_tok = p.n_tok;
   a.n_kv = p.n_kv;
   a.M = M;
+  a.n_kvh = p.n_kvh;
+  a.grp = p.grp();
   a.n_split = plan.n_split;
   a.chunk = plan.chunk;
   a.n_rowblk = plan.n_rowblk;
   a.tpr = plan.tpr;
   a.scale = p.scale;
-  const size_t part_o_bytes = (size_t)p.n_inst * plan.n_split * M * p.hd * sizeof(float);
+  const size_t part_o_bytes = (size_t)p.units() * plan.n_split * M * p.hd * sizeof(float);
   a.part_o = plan.n_split > 1 ? (float *)workspace : nullptr;
   a.part_ml = plan.n_split > 1 ? (float2v *)((char *)workspace + part_o_bytes) : nullptr;
 
@@ -1004,7 +1019,10 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   c.out_stride = p.out_stride;
   c.M = M;
   c.n_split = plan.n_split;
-  c.n_inst = p.n_inst;
+  c.n_inst = p.units();
+  c.n_kvh = p.n_kvh;
+  c.grp = p.grp();
+  c.n_head = p.n_head;
   switch (p.hd) {
     case 64: return launch_combine<64>(c, stream);
     case 128: return launch_combine<128>(c, stream);

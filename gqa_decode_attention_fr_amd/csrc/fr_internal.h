@@ -30,6 +30,13 @@ struct Plan {
 };
 
 // Everything one launch sequence needs.  Strides count elements.
+//
+// KV-head groups: each instance has n_kvh KV heads, and query head h reads KV
+// head h / (n_head / n_kvh) (consecutive query heads share one).  The kernels
+// work on units u = inst * n_kvh + kv, one per (instance, KV head), each with
+// grp = n_head / n_kvh query heads and grp * n_tok rows ordered t-major inside
+// the unit; unit row rho = t*grp + j is row t*n_head + kv*grp + j of the
+// instance.  With one KV head a unit is an instance and the rows coincide.
 struct Problem {
   const void *q;
   const uint16_t *k;
@@ -39,8 +46,13 @@ struct Problem {
   int n_inst;
   int64_t q_stride, kv_stride, mask_stride, out_stride;
   int n_head, n_tok, n_kv, hd;
+  int n_kvh;            // KV heads per instance (divides n_head)
+  int64_t kvh_stride;   // elements between consecutive KV heads of K (and V)
   float scale;
   int qmode;
+  int grp() const { return n_head / n_kvh; }
+  int units() const { return n_inst * n_kvh; }
+  int unit_rows() const { return grp() * n_tok; }
 };
 
 // Integer environment override (developer knobs; fallback when unset).

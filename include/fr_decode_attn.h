@@ -74,7 +74,7 @@ extern "C" {
 /* Status codes. */
 typedef enum fr_status {
     FR_OK = 0,
-    FR_ERR_INVALID = -1,     /* null/misaligned pointer, bad size or stride, out overlaps an input */
+    FR_ERR_INVALID = -1,     /* null/misaligned pointer, bad size, stride or KV-head count, out overlaps an input */
     FR_ERR_UNSUPPORTED = -2, /* n_tok outside 1..16, hd not 64/128/256, n_head outside 1..1024 */
     FR_ERR_CAPTURE = -3,     /* the library workspace would have to grow while the stream is captured */
     FR_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
@@ -144,6 +144,38 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k,
                       int64_t mask_stride, int64_t out_stride, int n_head,
                       int n_tok, int n_kv, int hd, float scale, unsigned flags,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Several KV heads (grouped-query attention with n_kv_head groups).  The pages
+ * fix one KV head shared by every query head; this entry point widens the
+ * same window to n_kv_head KV heads, with query head h attending over KV head
+ * h / (n_head / n_kv_head) (consecutive query heads share a KV head, the
+ * flash-attention node's broadcast of KV heads over query heads):
+ *
+ *     s_j           = scale * sum_e q[t][h][e] * K[h/G][j][e] + mask[t][j]
+ *     out[t][h][d]  = softmax_j(s)_j-weighted sum of V[h/G][j][d],   G = n_head/n_kv_head
+ *
+ * q, mask and out keep the layouts above (t-major rows over all n_head heads,
+ * one mask row per token shared by every head).  k and v of one instance are
+ * n_kv_head blocks of [n_kv][hd], block kh at k + kh*kv_head_stride (ELEMENTS;
+ * at least n_kv*hd and a multiple of 8 when n_kv_head > 1, ignored when it is
+ * 1).  kv_stride between instances, when not 0, must cover all n_kv_head
+ * blocks.  n_kv_head must divide n_head, else FR_ERR_INVALID.  Every other
+ * argument, flag and rule is that of fr_decode_attn_ex, which is this call
+ * with n_kv_head = 1.
+ *
+ * Planning: the call runs as n_inst*n_kv_head units of n_head/n_kv_head query
+ * heads each, so fr_decode_attn_workspace_size, fr_decode_attn_reserve and
+ * fr_decode_attn_plan take (n_inst*n_kv_head, n_head/n_kv_head, n_tok, n_kv,
+ * hd, flags) for it.
+ */
+int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k,
+                       const uint16_t *v, const uint16_t *mask, float *out,
+                       int n_inst, int64_t q_stride, int64_t kv_stride,
+                       int64_t mask_stride, int64_t out_stride, int n_head,
+                       int n_kv_head, int64_t kv_head_stride, int n_tok, int n_kv,
+                       int hd, float scale, unsigned flags, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Device workspace bytes a call with these sizes and flags needs (0 if none),
  * or 0 with *status set when the sizes are rejected (status may be NULL).

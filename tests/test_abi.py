@@ -96,6 +96,40 @@ def test_rejected_before_any_launch(kw, status):
     assert call(**kw) == status
 
 
+def gqa_call(**kw):
+    a = dict(q=Q, fmt=B.FR_Q_F32, k=K, v=V, mask=MASK, out=OUT, n_inst=1, qs=0, kvs=0, ms=0,
+             os_=0, n_head=8, n_kvh=2, kvhs=1024 * 128, n_tok=4, n_kv=1024, hd=128,
+             scale=0.088, flags=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return B.load().fr_decode_attn_gqa(a["q"], a["fmt"], a["k"], a["v"], a["mask"], a["out"],
+                                       a["n_inst"], a["qs"], a["kvs"], a["ms"], a["os_"],
+                                       a["n_head"], a["n_kvh"], a["kvhs"], a["n_tok"], a["n_kv"],
+                                       a["hd"], a["scale"], a["flags"], a["ws"], a["ws_bytes"],
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_kvh=0), B.FR_ERR_INVALID),
+    (dict(n_kvh=3), B.FR_ERR_INVALID),                       # does not divide n_head
+    (dict(n_kvh=16), B.FR_ERR_INVALID),
+    (dict(kvhs=1024 * 128 - 8), B.FR_ERR_INVALID),           # heads would overlap
+    (dict(kvhs=1024 * 128 + 4), B.FR_ERR_INVALID),           # breaks 16-byte alignment
+    (dict(n_inst=2, os_=32 * 128, kvs=1024 * 128), B.FR_ERR_INVALID),  # instance < 2 heads
+    (dict(out=K + 1024 * 128 * 2), B.FR_ERR_INVALID),        # out inside the second KV head
+    (dict(n_tok=17), B.FR_ERR_UNSUPPORTED),
+    (dict(q=None), B.FR_ERR_INVALID),
+])
+def test_gqa_rejected_before_any_launch(kw, status):
+    assert gqa_call(**kw) == status
+
+
+def test_gqa_with_one_kv_head_validates_like_ex():
+    # one KV head ignores the head stride; the rest of the checks are shared
+    for kw in (dict(n_tok=17), dict(hd=96), dict(out=Q), dict(scale=float("nan"))):
+        a = dict(kw)
+        assert gqa_call(n_kvh=1, kvhs=-5, **a) == call(**a)
+
+
 def test_single_entry_points_validate_too():
     lib = B.load()
     assert lib.fr_decode_attn(None, K, V, MASK, OUT, 8, 1, 64, 256, 0.0625, None) == B.FR_ERR_INVALID

@@ -1,0 +1,135 @@
+"""GPU parity of the several-KV-head entry point (fr_decode_attn_gqa): query
+head h attends over KV head h // (n_head // n_kv_head).  Checked against the
+fp64 oracle at the acceptance tolerance, and bit for bit against separate
+one-KV-head calls on each group's query heads with the same key splits."""
+import math
+
+import numpy as np
+import pytest
+
+from gqa_decode_attention_fr_amd import workloads as W
+from gpu_util import assert_close, dev, errors, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+FUSED, DECOMP = 0x2, 0x4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_decode_attention_fr_amd as F
+    F.binding.load()
+    yield
+
+
+def _padded_kv(x, pad_rows, fill):
+    """[n_inst, n_kvh, n_kv, hd] -> the same with pad_rows extra rows per KV
+    head holding `fill` (f16 bits), which the kernels must never read."""
+    if pad_rows == 0:
+        return x
+    n_inst, n_kvh, n_kv, hd = x.shape
+    out = np.full((n_inst, n_kvh, n_kv + pad_rows, hd), fill, dtype=np.uint16)
+    out[:, :, :n_kv] = x
+    return out
+
+
+def run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=0, q_f16=False, pad_rows=0):
+    import gqa_decode_attention_fr_amd as F
+    n_inst = c["q"].shape[0]
+    kf = _padded_kv(c["k"], pad_rows, 0x7BFF)     # 65504: huge if ever read
+    vf = _padded_kv(c["v"], pad_rows, 0x7BFF)
+    q, k, v, mask = dev(c["q"], torch), dev(kf, torch), dev(vf, torch), dev(c["mask"], torch)
+    M = n_head * n_tok
+    kvh_stride = (n_kv + pad_rows) * hd
+    out = torch.full((n_inst, n_tok, n_head, hd), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    F.fr_decode_attn_gqa(q, F.FR_Q_F16 if q_f16 else F.FR_Q_F32, k, v, mask, out, n_inst,
+                         M * hd, n_kvh * kvh_stride, 0 if mask is None else n_tok * n_kv,
+                         M * hd, n_head, n_kvh, kvh_stride, n_tok, n_kv, hd, scale, flags)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_gqa(oracle, c, n_head, n_kvh, n_tok, n_kv, hd, scale, q_kind):
+    outs = []
+    for i in range(c["q"].shape[0]):
+        m = None if c["mask"] is None else c["mask"][i]
+        outs.append(oracle.decode_attn(c["q"][i], c["k"][i], c["v"][i], m, n_head, n_tok, n_kv,
+                                       hd, scale, q_kind=q_kind, n_kv_head=n_kvh))
+    return np.stack(outs)
+
+
+GQA = [  # n_inst, n_head, n_kv_head, n_tok, n_kv, hd, q dtype, mask kind, pad rows per KV head
+    (2, 32, 8, 4, 1000, 128, "f32", "random", 0),      # 4 query heads per KV head
+    (1, 16, 2, 16, 4096, 128, "f16", "zero", 0),
+    (3, 8, 8, 10, 333, 64, "f32", "random", 0),       # one query head per KV head
+    (1, 28, 4, 1, 2048, 128, "f32", "none", 0),       # single-token decode, 7 per group
+    (2, 12, 3, 16, 777, 256, "f32", "full_row", 0),
+    (1, 64, 8, 16, 8192, 128, "f32", "random", 0),    # 128 rows per unit
+    (2, 8, 2, 10, 968, 256, "f32", "random", 56),     # padded head stride
+    (1, 40, 5, 3, 1531, 64, "f16", "random", 8),
+]
+
+
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+@pytest.mark.parametrize("shape", GQA, ids=lambda s: "n{}_h{}_g{}_t{}_kv{}_d{}_{}_{}_p{}".format(*s))
+def test_gqa_parity(oracle_mod, shape, variant):
+    n_inst, n_head, n_kvh, n_tok, n_kv, hd, qd, mk, pad = shape
+    say(f"gqa {shape} variant={variant}")
+    c = W.random_case(GQA.index(shape) + 500, n_head, n_tok, n_kv, hd, q_dtype=qd,
+                      mask_kind=mk, n_inst=n_inst, n_kv_head=n_kvh)
+    if n_kvh == 1:
+        c["k"], c["v"] = c["k"][:, None], c["v"][:, None]
+    scale = 1.0 / math.sqrt(hd)
+    got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=variant,
+                  q_f16=(qd == "f16"), pad_rows=pad)
+    want = oracle_gqa(oracle_mod, c, n_head, n_kvh, n_tok, n_kv, hd, scale,
+                      oracle_mod.Q_F16 if qd == "f16" else oracle_mod.Q_F32)
+    max_abs, rel = errors(got, want)
+    print(f"[parity] gqa {shape} variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got, want, str(shape))
+    if mk == "full_row":
+        assert np.array_equal(got[:, 0], np.zeros_like(got[:, 0]))
+
+
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+def test_gqa_equals_one_call_per_group(monkeypatch, variant):
+    """Each group of query heads through the one-KV-head entry point, with the
+    key splits forced equal: the grouped call must match bit for bit (only
+    where rows are read and written differs)."""
+    import gqa_decode_attention_fr_amd as F
+    n_inst, n_head, n_kvh, n_tok, n_kv, hd = 2, 24, 4, 7, 1500, 128
+    G = n_head // n_kvh
+    say(f"gqa per-group identity variant={variant}")
+    monkeypatch.setenv("FR_FORCE_SPLITS", "6")
+    c = W.random_case(601, n_head, n_tok, n_kv, hd, mask_kind="random", n_inst=n_inst,
+                      n_kv_head=n_kvh)
+    scale = 1.0 / math.sqrt(hd)
+    got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=variant)
+    for i in range(n_inst):
+        for kh in range(n_kvh):
+            qg = np.ascontiguousarray(c["q"][i][:, kh * G:(kh + 1) * G, :])
+            out = torch.full((n_tok, G, hd), float("nan"), dtype=torch.float32, device="cuda")
+            F.fr_decode_attn_ex(dev(qg, torch), F.FR_Q_F32, dev(c["k"][i, kh], torch),
+                                dev(c["v"][i, kh], torch), dev(c["mask"][i], torch), out, 1,
+                                0, 0, 0, 0, G, n_tok, n_kv, hd, scale, variant)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), got[i][:, kh * G:(kh + 1) * G, :]), \
+                f"instance {i} KV head {kh}"
+
+
+def test_gqa_with_one_kv_head_equals_ex():
+    """n_kv_head = 1 is the pages' window: the same bits as fr_decode_attn_ex."""
+    import gqa_decode_attention_fr_amd as F
+    w = W.PI05_ACTION_STEP
+    say("gqa one KV head == ex")
+    g = W.generate(w)
+    c = dict(g)
+    c["k"], c["v"] = g["k"][:, None], g["v"][:, None]
+    got = run_gqa(c, w.n_head, 1, w.n_tok, w.n_kv, w.hd, w.scale)
+    from gpu_util import run_gpu
+    ref = run_gpu(g, w.n_head, w.n_tok, w.n_kv, w.hd, w.scale, torch=torch)
+    assert np.array_equal(got, ref)
