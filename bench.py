@@ -98,19 +98,27 @@ class Pool:
 
 
 def make_call(F, w, pool, flags):
+    """One call over the whole batch: fr_decode_attn_ex, or fr_decode_attn_gqa
+    for workloads with several KV heads."""
     fmt = F.FR_Q_F16 if w.q_dtype == "f16" else F.FR_Q_F32
     M = w.M
     lib = F.binding.load()
-    qs, ks, ms, os_ = M * w.hd, w.n_kv * w.hd, w.n_tok * w.n_kv, M * w.hd
+    kvh_stride = w.n_kv * w.hd
+    qs, ks, ms, os_ = M * w.hd, w.n_kv_head * kvh_stride, w.n_tok * w.n_kv, M * w.hd
     ptrs = [(pool.q[r].data_ptr(), pool.k[r].data_ptr(), pool.v[r].data_ptr(),
              pool.mask[r].data_ptr(), pool.out[r].data_ptr()) for r in range(pool.R)]
 
     def call(slot, stream):
         q, k, v, m, o = ptrs[slot]
-        st = lib.fr_decode_attn_ex(q, fmt, k, v, m, o, w.n_inst, qs, ks, ms, os_, w.n_head,
-                                   w.n_tok, w.n_kv, w.hd, w.scale, flags, None, 0, stream)
+        if w.n_kv_head == 1:
+            st = lib.fr_decode_attn_ex(q, fmt, k, v, m, o, w.n_inst, qs, ks, ms, os_, w.n_head,
+                                       w.n_tok, w.n_kv, w.hd, w.scale, flags, None, 0, stream)
+        else:
+            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, o, w.n_inst, qs, ks, ms, os_,
+                                        w.n_head, w.n_kv_head, kvh_stride, w.n_tok, w.n_kv,
+                                        w.hd, w.scale, flags, None, 0, stream)
         if st != 0:
-            raise F.FrError(st, "fr_decode_attn_ex")
+            raise F.FrError(st, "decode attention call")
 
     return call
 
@@ -121,8 +129,9 @@ def make_single_calls(F, w, pool, flags):
     M = w.M
     lib = F.binding.load()
     qe = 2 if w.q_dtype == "f16" else 4
-    steps = (M * w.hd * qe, w.n_kv * w.hd * 2, w.n_kv * w.hd * 2, w.n_tok * w.n_kv * 2,
-             M * w.hd * 4)
+    kvh_stride = w.n_kv * w.hd
+    steps = (M * w.hd * qe, w.n_kv_head * kvh_stride * 2, w.n_kv_head * kvh_stride * 2,
+             w.n_tok * w.n_kv * 2, M * w.hd * 4)
     ptrs = [(pool.q[r].data_ptr(), pool.k[r].data_ptr(), pool.v[r].data_ptr(),
              pool.mask[r].data_ptr(), pool.out[r].data_ptr()) for r in range(pool.R)]
 
@@ -130,10 +139,11 @@ def make_single_calls(F, w, pool, flags):
         base = ptrs[slot]
         for i in range(w.n_inst):
             q, k, v, m, o = (b + i * d for b, d in zip(base, steps))
-            st = lib.fr_decode_attn_ex(q, fmt, k, v, m, o, 1, 0, 0, 0, 0, w.n_head, w.n_tok,
-                                       w.n_kv, w.hd, w.scale, flags, None, 0, stream)
+            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, o, 1, 0, 0, 0, 0, w.n_head,
+                                        w.n_kv_head, kvh_stride, w.n_tok, w.n_kv, w.hd,
+                                        w.scale, flags, None, 0, stream)
             if st != 0:
-                raise F.FrError(st, "fr_decode_attn_ex")
+                raise F.FrError(st, "fr_decode_attn_gqa")
 
     return call
 
@@ -258,7 +268,8 @@ def cpu_baseline(w, g, gpu_out, repeats):
         for i in range(w.n_inst):
             o, threads = oracle.decode_attn(g["q"][i], g["k"][i], g["v"][i], g["mask"][i],
                                             w.n_head, w.n_tok, w.n_kv, w.hd, w.scale,
-                                            q_kind=q_kind, return_threads=True)
+                                            q_kind=q_kind, return_threads=True,
+                                            n_kv_head=w.n_kv_head)
             res.append(o)
         times.append(time.perf_counter() - t)
         out = np.stack(res)
@@ -276,10 +287,12 @@ def run_workload(args, torch, F, W, w):
              "decomposed": F.FR_VARIANT_DECOMPOSED}[args.variant]
     if args.round_f16:
         flags |= F.FR_Q_ROUND_F16
-    plan = F.fr_decode_attn_plan(w.n_inst, w.n_head, w.n_tok, w.n_kv, w.hd, flags)
+    # several KV heads run as n_inst*n_kv_head units of n_head/n_kv_head heads
+    units, grp = w.n_inst * w.n_kv_head, w.n_head // w.n_kv_head
+    plan = F.fr_decode_attn_plan(units, grp, w.n_tok, w.n_kv, w.hd, flags)
     g = W.generate(w)
     pool = Pool(torch, w, g, args.pool_gib * (1 << 30))
-    F.fr_decode_attn_reserve(w.n_inst, w.n_head, w.n_tok, w.n_kv, w.hd, flags)
+    F.fr_decode_attn_reserve(units, grp, w.n_tok, w.n_kv, w.hd, flags)
     call = make_call(F, w, pool, flags)
     stream = int(torch.cuda.current_stream().cuda_stream)
 
@@ -349,7 +362,7 @@ def run_workload(args, torch, F, W, w):
             " (f32 Q as hi+lo f16)" if w.q_dtype == "f32" and not args.round_f16 else ""),
         "data": "synthetic (seeded normal Q/K/V, f16 0/-inf masks; no checkpoint)",
         "config": {"workload": w.name, "n_inst": w.n_inst, "n_head": w.n_head,
-                   "n_tok": w.n_tok, "n_kv": w.n_kv, "n_valid": w.n_valid, "hd": w.hd,
+                   "n_kv_head": w.n_kv_head, "n_tok": w.n_tok, "n_kv": w.n_kv, "n_valid": w.n_valid, "hd": w.hd,
                    "q_dtype": w.q_dtype, "variant": args.variant,
                    "round_f16": bool(args.round_f16)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -394,7 +407,8 @@ def main(argv=None):
         calibrate_copy(torch, args.steps)
         return 0
     F.binding.load()
-    names = [w.name for w in W.WORKLOADS] if args.workload == "all" else [args.workload]
+    names = ([w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS] if args.workload == "all"
+             else [args.workload])
     for name in names:
         if name not in W.BY_NAME:
             print(f"unknown workload {name}; choose from {list(W.BY_NAME)}", file=sys.stderr)

@@ -17,6 +17,7 @@ Draw order per instance, from ``numpy.random.default_rng(seed)`` (PCG64):
   1. Q  = standard_normal((n_tok, n_head, hd)) * sigma_q, float64 -> float32
          (f16 workloads then round float32 -> float16, nearest-even)
   2. K  = standard_normal((n_valid, hd)) * sigma_kv, float64 -> float16
+         (several KV heads: standard_normal((n_kv_head, n_valid, hd)))
   3. V  = same as K
   4. extras: the outlier rows of K (chosen without replacement, scaled in f16)
 Then the n_kv - n_valid pad rows are appended as zeros and the mask is built.
@@ -49,6 +50,7 @@ class Workload:
     k_outlier_frac: float = 0.0
     k_outlier_scale: float = 1.0
     seed: int = 0
+    n_kv_head: int = 1   # KV heads; query head h reads KV head h // (n_head // n_kv_head)
 
     @property
     def scale(self) -> float:
@@ -63,7 +65,7 @@ class Workload:
         K and V over keys visible to at least one query, Q, the full mask,
         and the fp32 output."""
         qb = 4 if self.q_dtype == "f32" else 2
-        per = (2 * self.n_valid * self.hd * 2 + self.M * self.hd * qb
+        per = (2 * self.n_kv_head * self.n_valid * self.hd * 2 + self.M * self.hd * qb
                + self.n_tok * self.n_kv * 2 + self.M * self.hd * 4)
         return per * self.n_inst
 
@@ -86,7 +88,15 @@ LONG_CONTEXT = Workload("long_context_h32_hd128_t16_kv32768", n_head=32, n_tok=1
                         n_kv=32768, n_valid=32000, hd=128, mask_kind="pad")
 
 WORKLOADS = [TINY, PI05_ACTION_STEP, H16_HD128_Q16, CAUSAL_TAIL, LONG_CONTEXT]
-BY_NAME = {w.name: w for w in WORKLOADS}
+
+# Beyond the pages' one KV head: grouped-query decode with 8 KV heads of 4
+# query heads each, 4 query tokens (a short speculative-verify window), 4096
+# keys, 8 independent sequences per call.
+GQA_KV8 = Workload("gqa_h32_kv8_hd128_t4_kv4096_x8", n_head=32, n_tok=4, n_kv=4096,
+                   n_valid=4096, hd=128, n_inst=8, n_kv_head=8)
+EXTRA_WORKLOADS = [GQA_KV8]
+
+BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def f16_bits(x: np.ndarray) -> np.ndarray:
@@ -117,21 +127,27 @@ def generate(w: Workload, seed: int | None = None) -> dict:
 
     Returns a dict with
       q    [n_inst, n_tok, n_head, hd] float32, or uint16 f16 bits if q_dtype == "f16"
-      k, v [n_inst, n_kv, hd] uint16 f16 bits (pad rows zero)
+      k, v [n_inst, n_kv, hd] uint16 f16 bits (pad rows zero); with several KV
+           heads [n_inst, n_kv_head, n_kv, hd]
       mask [n_inst, n_tok, n_kv] uint16 f16 bits
       outlier_rows [n_inst, n_outliers] int64 (empty when there are none)
     """
     rng = np.random.default_rng(w.seed if seed is None else seed)
     n_out = int(round(w.k_outlier_frac * w.n_valid))
+    if n_out and w.n_kv_head != 1:
+        raise ValueError("outlier rows are defined for one KV head only")
     qs, ks, vs, outs = [], [], [], []
     for _ in range(w.n_inst):
         q = (rng.standard_normal((w.n_tok, w.n_head, w.hd)) * w.sigma_q).astype(np.float32)
         if w.q_dtype == "f16":
             q = f16_bits(q)
-        k = np.zeros((w.n_kv, w.hd), dtype=np.uint16)
-        v = np.zeros((w.n_kv, w.hd), dtype=np.uint16)
-        k[:w.n_valid] = f16_bits(rng.standard_normal((w.n_valid, w.hd)) * w.sigma_kv)
-        v[:w.n_valid] = f16_bits(rng.standard_normal((w.n_valid, w.hd)) * w.sigma_kv)
+        heads = () if w.n_kv_head == 1 else (w.n_kv_head,)
+        k = np.zeros(heads + (w.n_kv, w.hd), dtype=np.uint16)
+        v = np.zeros(heads + (w.n_kv, w.hd), dtype=np.uint16)
+        k[..., :w.n_valid, :] = f16_bits(
+            rng.standard_normal(heads + (w.n_valid, w.hd)) * w.sigma_kv)
+        v[..., :w.n_valid, :] = f16_bits(
+            rng.standard_normal(heads + (w.n_valid, w.hd)) * w.sigma_kv)
         rows = np.zeros((0,), dtype=np.int64)
         if n_out:
             rows = np.sort(rng.choice(w.n_valid, size=n_out, replace=False))

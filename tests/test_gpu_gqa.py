@@ -133,3 +133,17 @@ def test_gqa_with_one_kv_head_equals_ex():
     from gpu_util import run_gpu
     ref = run_gpu(g, w.n_head, w.n_tok, w.n_kv, w.hd, w.scale, torch=torch)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+def test_gqa_workload_full_size(oracle_mod, variant):
+    """The measured several-KV-head workload, every element, both variants."""
+    w = W.GQA_KV8
+    say(f"workload {w.name} variant={variant}")
+    g = W.generate(w)
+    got = run_gqa(g, w.n_head, w.n_kv_head, w.n_tok, w.n_kv, w.hd, w.scale, flags=variant)
+    want = oracle_gqa(oracle_mod, g, w.n_head, w.n_kv_head, w.n_tok, w.n_kv, w.hd, w.scale,
+                      oracle_mod.Q_F32)
+    max_abs, rel = errors(got, want)
+    print(f"[parity] {w.name} variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got, want, w.name)

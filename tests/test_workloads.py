@@ -82,3 +82,16 @@ def test_byte_and_flop_accounting():
     kv = 2 * 32000 * 128 * 2
     assert w.algorithmic_bytes() == kv + 512 * 128 * 4 + 16 * 32768 * 2 + 512 * 128 * 4
     assert w.flops() == 4 * 512 * 32000 * 128
+
+
+def test_several_kv_head_workload():
+    w = W.GQA_KV8
+    g = W.generate(w)
+    assert g["k"].shape == g["v"].shape == (w.n_inst, w.n_kv_head, w.n_kv, w.hd)
+    assert g["q"].shape == (w.n_inst, w.n_tok, w.n_head, w.hd)
+    assert w.n_head % w.n_kv_head == 0 and w.M == 128
+    # every KV head holds its own draws
+    assert not np.array_equal(g["k"][0, 0], g["k"][0, 1])
+    assert w.algorithmic_bytes() == w.n_inst * (2 * 8 * 4096 * 128 * 2 + 128 * 128 * 4
+                                                + 4 * 4096 * 2 + 128 * 128 * 4)
+    assert w.name in W.BY_NAME and w not in W.WORKLOADS
