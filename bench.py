@@ -114,7 +114,7 @@ def make_call(F, w, pool, flags):
             st = lib.fr_decode_attn_ex(q, fmt, k, v, m, o, w.n_inst, qs, ks, ms, os_, w.n_head,
                                        w.n_tok, w.n_kv, w.hd, w.scale, flags, None, 0, stream)
         else:
-            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, o, w.n_inst, qs, ks, ms, os_,
+            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, None, o, w.n_inst, qs, ks, ms, os_,
                                         w.n_head, w.n_kv_head, kvh_stride, w.n_tok, w.n_kv,
                                         w.hd, w.scale, flags, None, 0, stream)
         if st != 0:
@@ -139,7 +139,7 @@ def make_single_calls(F, w, pool, flags):
         base = ptrs[slot]
         for i in range(w.n_inst):
             q, k, v, m, o = (b + i * d for b, d in zip(base, steps))
-            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, o, 1, 0, 0, 0, 0, w.n_head,
+            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, None, o, 1, 0, 0, 0, 0, w.n_head,
                                         w.n_kv_head, kvh_stride, w.n_tok, w.n_kv, w.hd,
                                         w.scale, flags, None, 0, stream)
             if st != 0:

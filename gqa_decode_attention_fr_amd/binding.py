@@ -68,8 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     batched = [vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, i32, i32, i32, f32]
     lib.fr_decode_attn_batched.argtypes = batched + [vp]
     lib.fr_decode_attn_ex.argtypes = batched + [u32, vp, sz, vp]
-    lib.fr_decode_attn_gqa.argtypes = (batched[:12] + [i32, i64] + batched[12:] +
-                                       [u32, vp, sz, vp])
+    lib.fr_decode_attn_gqa.argtypes = (batched[:5] + [vp] + batched[5:12] + [i32, i64] +
+                                       batched[12:] + [u32, vp, sz, vp])
     for fn in ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
                "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_reserve",
                "fr_decode_attn_plan",
@@ -150,12 +150,14 @@ def fr_decode_attn_ex(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride,
 
 def fr_decode_attn_gqa(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride,
                        out_stride, n_head, n_kv_head, kv_head_stride, n_tok, n_kv, hd, scale,
-                       flags=0, workspace=None, workspace_bytes=0, stream=None) -> None:
+                       flags=0, workspace=None, workspace_bytes=0, stream=None,
+                       kv_len=None) -> None:
     """As fr_decode_attn_ex with n_kv_head KV heads per instance ([n_kv_head, n_kv, hd]
     blocks kv_head_stride elements apart); query head h reads KV head
-    h // (n_head // n_kv_head)."""
+    h // (n_head // n_kv_head).  kv_len: None or a device int32 tensor of n_inst
+    valid key counts."""
     _check(load().fr_decode_attn_gqa(_ptr(q), q_format, _ptr(k), _ptr(v), _ptr(mask),
-                                     _ptr(out), n_inst, q_stride, kv_stride, mask_stride,
+                                     _ptr(kv_len), _ptr(out), n_inst, q_stride, kv_stride, mask_stride,
                                      out_stride, n_head, n_kv_head, kv_head_stride, n_tok, n_kv,
                                      hd, scale, flags, _ptr(workspace), workspace_bytes,
                                      _stream(stream)), "fr_decode_attn_gqa")

@@ -238,19 +238,22 @@ int library_ws(size_t need, hipStream_t stream, bool check_capture, void **out) 
 }
 
 int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const uint16_t *mask,
-        float *out, int n_inst, int64_t q_stride, int64_t kv_stride, int64_t mask_stride,
+        const int32_t *kv_len, float *out, int n_inst, int64_t q_stride, int64_t kv_stride, int64_t mask_stride,
         int64_t out_stride, int n_head, int n_kvh, int64_t kvh_stride, int n_tok, int n_kv,
         int hd, float scale, unsigned flags, void *workspace, size_t workspace_bytes,
         bool caller_ws, void *stream) {
   int st = validate(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride,
                     out_stride, n_head, n_kvh, kvh_stride, n_tok, n_kv, hd, scale, flags);
   if (st != FR_OK) return st;
+  if (kv_len && !aligned(kv_len, 4)) return FR_ERR_INVALID;
   if (n_inst == 1) q_stride = kv_stride = mask_stride = out_stride = 0;
   if (n_kvh == 1) kvh_stride = 0;
   // the kernels run on units (instance, KV head) of n_head / n_kvh query heads
   Plan plan;
   st = fr::make_plan(n_inst * n_kvh, n_head / n_kvh, n_tok, n_kv, hd, flags, &plan);
   if (st != FR_OK) return st;
+  // a device-side key count is honoured by the fused path only
+  if (kv_len && plan.variant == fr::kDecomposed) return FR_ERR_UNSUPPORTED;
   if (caller_ws) {
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
       return FR_ERR_WORKSPACE;
@@ -264,6 +267,7 @@ int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const
   p.k = k;
   p.v = v;
   p.mask = mask;
+  p.kv_len = kv_len;
   p.out = out;
   p.n_inst = n_inst;
   p.q_stride = q_stride;
@@ -297,14 +301,14 @@ extern "C" {
 int fr_decode_attn(const float *q, const uint16_t *k, const uint16_t *v, const uint16_t *mask,
                    float *out, int n_head, int n_tok, int n_kv, int hd, float scale,
                    void *stream) {
-  return run(q, FR_Q_F32, k, v, mask, out, 1, 0, 0, 0, 0, n_head, 1, 0, n_tok, n_kv, hd, scale,
+  return run(q, FR_Q_F32, k, v, mask, nullptr, out, 1, 0, 0, 0, 0, n_head, 1, 0, n_tok, n_kv, hd, scale,
              0u, nullptr, 0, false, stream);
 }
 
 int fr_decode_attn_q16(const uint16_t *q16, const uint16_t *k, const uint16_t *v,
                        const uint16_t *mask, float *out, int n_head, int n_tok, int n_kv, int hd,
                        float scale, void *stream) {
-  return run(q16, FR_Q_F16, k, v, mask, out, 1, 0, 0, 0, 0, n_head, 1, 0, n_tok, n_kv, hd,
+  return run(q16, FR_Q_F16, k, v, mask, nullptr, out, 1, 0, 0, 0, 0, n_head, 1, 0, n_tok, n_kv, hd,
              scale, 0u, nullptr, 0, false, stream);
 }
 
@@ -312,8 +316,8 @@ int fr_decode_attn_batched(const void *q, int q_format, const uint16_t *k, const
                            const uint16_t *mask, float *out, int n_inst, int64_t q_stride,
                            int64_t kv_stride, int64_t mask_stride, int64_t out_stride,
                            int n_head, int n_tok, int n_kv, int hd, float scale, void *stream) {
-  return run(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride, out_stride,
-             n_head, 1, 0, n_tok, n_kv, hd, scale, 0u, nullptr, 0, false, stream);
+  return run(q, q_format, k, v, mask, nullptr, out, n_inst, q_stride, kv_stride, mask_stride,
+             out_stride, n_head, 1, 0, n_tok, n_kv, hd, scale, 0u, nullptr, 0, false, stream);
 }
 
 int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
@@ -321,19 +325,20 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k, const uint
                       int64_t kv_stride, int64_t mask_stride, int64_t out_stride, int n_head,
                       int n_tok, int n_kv, int hd, float scale, unsigned flags, void *workspace,
                       size_t workspace_bytes, void *stream) {
-  return run(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride, out_stride,
-             n_head, 1, 0, n_tok, n_kv, hd, scale, flags, workspace, workspace_bytes,
-             workspace != nullptr, stream);
+  return run(q, q_format, k, v, mask, nullptr, out, n_inst, q_stride, kv_stride, mask_stride,
+             out_stride, n_head, 1, 0, n_tok, n_kv, hd, scale, flags, workspace,
+             workspace_bytes, workspace != nullptr, stream);
 }
 
 int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
-                       const uint16_t *mask, float *out, int n_inst, int64_t q_stride,
+                       const uint16_t *mask, const int32_t *kv_len, float *out, int n_inst,
+                       int64_t q_stride,
                        int64_t kv_stride, int64_t mask_stride, int64_t out_stride, int n_head,
                        int n_kv_head, int64_t kv_head_stride, int n_tok, int n_kv, int hd,
                        float scale, unsigned flags, void *workspace, size_t workspace_bytes,
                        void *stream) {
-  return run(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride, out_stride,
-             n_head, n_kv_head, kv_head_stride, n_tok, n_kv, hd, scale, flags, workspace,
+  return run(q, q_format, k, v, mask, kv_len, out, n_inst, q_stride, kv_stride, mask_stride,
+             out_stride, n_head, n_kv_head, kv_head_stride, n_tok, n_kv, hd, scale, flags, workspace,
              workspace_bytes, workspace != nullptr, stream);
 }
 

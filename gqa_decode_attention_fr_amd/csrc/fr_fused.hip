@@ -59,6 +59,7 @@ struct SplitArgs {
   const uint16_t *k;
   const uint16_t *v;
   const uint16_t *mask;
+  const int32_t *kv_len;  // per instance valid key count (device), or null
   float *out;
   float *part_o;    // [units][n_split][M][hd] unnormalised partial outputs
   float2v *part_ml; // [units][n_split][M] (running max in log2 units, sum)
@@ -279,9 +280,35 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   const uint16_t *kbase = a.k + kv_off;
   const uint16_t *vbase = a.v + kv_off;
   const uint16_t *mbase = a.mask ? a.mask + (int64_t)rinst * a.mask_stride : nullptr;
+  // keys past the instance's valid count (read from device memory, so a
+  // replayed graph sees the current value) are hidden and never loaded; n_kv
+  // stays the mask's row stride
+  const int n_eff = a.kv_len ? __builtin_amdgcn_readfirstlane(
+                                   min(max(a.kv_len[rinst], 0), a.n_kv))
+                             : a.n_kv;
   const int key_begin = split * a.chunk;
-  const int key_end = min(key_begin + a.chunk, a.n_kv);
-  const int nblk = (key_end - key_begin + KB - 1) / KB;
+  const int key_end = min(key_begin + a.chunk, n_eff);
+  const int nblk = key_end > key_begin ? (key_end - key_begin + KB - 1) / KB : 0;
+
+  if (nblk == 0) {
+    // (uniform) no valid key in this split: a zero output (every key of the
+    // rows is hidden) or an empty partial that the combine weighs 0
+    for (int i = 0; i < TPW; ++i) {
+      const int r = (rowblk * a.tpr + wave + kWaves * i) * 16 + l16;
+      if (wave + kWaves * i >= a.tpr || r >= a.M) continue;
+      const float4v zero = {0.f, 0.f, 0.f, 0.f};
+      if (a.n_split == 1) {
+        float *orow = a.out + (int64_t)rinst * a.out_stride +
+                      (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD;
+        for (int dt = 0; dt < DT; ++dt) *(float4v *)(orow + dt * 16 + 4 * g) = zero;
+      } else {
+        const int64_t prow = ((int64_t)inst * a.n_split + split) * a.M + r;
+        for (int dt = 0; dt < DT; ++dt) *(float4v *)(a.part_o + prow * HD + dt * 16 + 4 * g) = zero;
+        if (g == 0) a.part_ml[prow] = float2v{-INFINITY, 0.f};
+      }
+    }
+    return;
+  }
 
   // register-staged mask values (kMaskReg only), loaded by inline assembly
   // and read only after the wait for their block
@@ -313,29 +340,29 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   // Issue every load of one 64-key block into stage `s`, in the order K,
   // mask, V: the last NJ vector-memory operations of a wave are its V loads,
   // so a wait for at most NJ outstanding operations has K and the mask.
-  // Blocks that reach past n_kv (at most the last) clamp their rows to a
-  // valid one and read the mask granules past n_kv from a valid address
+  // Blocks that reach past the valid keys (at most the last) clamp their rows
+  // to a valid one and read the mask granules past them from a valid address
   // (those keys are dropped by the ragged-block handling of the softmax).
   auto issue = [&](Stage<HD, NW> &s, int kb0, uint32_t (&rmr)[NMR]) __attribute__((always_inline)) {
-    const bool full = kb0 + KB <= a.n_kv;
+    const bool full = kb0 + KB <= n_eff;
     const char *kb = (const char *)(kbase + (int64_t)kb0 * HD);   // uniform
     const char *vb = (const char *)(vbase + (int64_t)kb0 * HD);
-    const int last = a.n_kv - 1 - kb0;                              // last valid row
-    uint32_t back[NJ];   // bytes from rows past n_kv back to the last key
+    const int last = n_eff - 1 - kb0;                               // last valid row
+    uint32_t back[NJ];   // bytes from rows past the valid keys back to the last one
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       back[j] = full ? 0u : 2u * (uint32_t)(max(dma_row[j] - last, 0) * HD);
       dma16(kb, dma_kofs[j] - back[j], (char *)s.k + (wave * NJ + j) * 1024);
     }
     if (MASKMODE == kMaskDma) {
-      const bool ok = m_tok < a.n_tok && (full || kb0 + 8 * m_gr < a.n_kv);
+      const bool ok = m_tok < a.n_tok && (full || kb0 + 8 * m_gr < n_eff);
       dma16((const char *)mbase, ok ? 2u * (uint32_t)kb0 + m_ofs : 0u, (char *)s.m + wave * 1024);
     } else if (MASKMODE == kMaskReg) {
 #pragma unroll
       for (int i = 0; i < NMR; ++i) {
         const int u = tid + i * kThreads;            // 1024 = 16 tokens x 64 keys
         const int t = u >> 6, j = u & 63;
-        const bool ok = t < a.n_tok && kb0 + j < a.n_kv;
+        const bool ok = t < a.n_tok && kb0 + j < n_eff;
         rmr[i] = gload_u16(mbase + (ok ? (int64_t)t * a.n_kv + kb0 + j : 0));
       }
     }
@@ -980,6 +1007,7 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   a.k = p.k;
   a.v = p.v;
   a.mask = p.mask;
+  a.kv_len = p.kv_len;
   a.out = p.out;
   a.q_stride = p.q_stride;
   a.kv_stride = p.kv_stride;

@@ -42,6 +42,7 @@ struct Problem {
   const uint16_t *k;
   const uint16_t *v;
   const uint16_t *mask;
+  const int32_t *kv_len;   // per instance valid key count (device), or null
   float *out;
   int n_inst;
   int64_t q_stride, kv_stride, mask_stride, out_stride;

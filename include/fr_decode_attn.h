@@ -146,9 +146,10 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Several KV heads (grouped-query attention with n_kv_head groups).  The pages
- * fix one KV head shared by every query head; this entry point widens the
- * same window to n_kv_head KV heads, with query head h attending over KV head
+ * Several KV heads (grouped-query attention with n_kv_head groups) and an
+ * optional device-side valid key count.  The pages fix one KV head shared by
+ * every query head; this entry point widens the same window to n_kv_head KV
+ * heads, with query head h attending over KV head
  * h / (n_head / n_kv_head) (consecutive query heads share a KV head, the
  * flash-attention node's broadcast of KV heads over query heads):
  *
@@ -168,9 +169,21 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k,
  * heads each, so fr_decode_attn_workspace_size, fr_decode_attn_reserve and
  * fr_decode_attn_plan take (n_inst*n_kv_head, n_head/n_kv_head, n_tok, n_kv,
  * hd, flags) for it.
+ *
+ * kv_len: NULL, or a DEVICE array of n_inst int32 valid key counts (4-byte
+ * aligned).  Instance i then behaves as if keys j >= kv_len[i] were hidden
+ * from every token (values below 0 count as 0, above n_kv as n_kv); their
+ * K, V and mask entries are never read.  The kernels read the array when
+ * they run, so a graph captured once replays with the counts the array holds
+ * at replay time, while n_kv (the padded capacity, the mask's row stride)
+ * stays fixed.  The key splits are planned for n_kv; splits past the valid
+ * count finish at once.  A row whose keys are all hidden is zero.  The
+ * decomposed variant does not take kv_len (FR_ERR_UNSUPPORTED with
+ * FR_VARIANT_DECOMPOSED).
  */
 int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k,
-                       const uint16_t *v, const uint16_t *mask, float *out,
+                       const uint16_t *v, const uint16_t *mask,
+                       const int32_t *kv_len, float *out,
                        int n_inst, int64_t q_stride, int64_t kv_stride,
                        int64_t mask_stride, int64_t out_stride, int n_head,
                        int n_kv_head, int64_t kv_head_stride, int n_tok, int n_kv,

@@ -99,9 +99,10 @@ def test_rejected_before_any_launch(kw, status):
 def gqa_call(**kw):
     a = dict(q=Q, fmt=B.FR_Q_F32, k=K, v=V, mask=MASK, out=OUT, n_inst=1, qs=0, kvs=0, ms=0,
              os_=0, n_head=8, n_kvh=2, kvhs=1024 * 128, n_tok=4, n_kv=1024, hd=128,
-             scale=0.088, flags=0, ws=None, ws_bytes=0)
+             scale=0.088, flags=0, ws=None, ws_bytes=0, kvl=None)
     a.update(kw)
-    return B.load().fr_decode_attn_gqa(a["q"], a["fmt"], a["k"], a["v"], a["mask"], a["out"],
+    return B.load().fr_decode_attn_gqa(a["q"], a["fmt"], a["k"], a["v"], a["mask"], a["kvl"],
+                                       a["out"],
                                        a["n_inst"], a["qs"], a["kvs"], a["ms"], a["os_"],
                                        a["n_head"], a["n_kvh"], a["kvhs"], a["n_tok"], a["n_kv"],
                                        a["hd"], a["scale"], a["flags"], a["ws"], a["ws_bytes"],
@@ -118,6 +119,8 @@ def gqa_call(**kw):
     (dict(out=K + 1024 * 128 * 2), B.FR_ERR_INVALID),        # out inside the second KV head
     (dict(n_tok=17), B.FR_ERR_UNSUPPORTED),
     (dict(q=None), B.FR_ERR_INVALID),
+    (dict(kvl=0x600002), B.FR_ERR_INVALID),                  # misaligned key counts
+    (dict(kvl=0x600000, flags=B.FR_VARIANT_DECOMPOSED), B.FR_ERR_UNSUPPORTED),
 ])
 def test_gqa_rejected_before_any_launch(kw, status):
     assert gqa_call(**kw) == status

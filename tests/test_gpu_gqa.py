@@ -1,7 +1,9 @@
 """GPU parity of the several-KV-head entry point (fr_decode_attn_gqa): query
 head h attends over KV head h // (n_head // n_kv_head).  Checked against the
 fp64 oracle at the acceptance tolerance, and bit for bit against separate
-one-KV-head calls on each group's query heads with the same key splits."""
+one-KV-head calls on each group's query heads with the same key splits.  Also
+its device-side valid key counts, against the oracle with those keys masked,
+eagerly and from one captured graph replayed with changing counts."""
 import math
 
 import numpy as np
@@ -36,11 +38,12 @@ def _padded_kv(x, pad_rows, fill):
     return out
 
 
-def run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=0, q_f16=False, pad_rows=0):
+def run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=0, q_f16=False, pad_rows=0,
+            kv_len=None, kv_override=None):
     import gqa_decode_attention_fr_amd as F
     n_inst = c["q"].shape[0]
-    kf = _padded_kv(c["k"], pad_rows, 0x7BFF)     # 65504: huge if ever read
-    vf = _padded_kv(c["v"], pad_rows, 0x7BFF)
+    kf = _padded_kv(c["k"] if kv_override is None else kv_override[0], pad_rows, 0x7BFF)
+    vf = _padded_kv(c["v"] if kv_override is None else kv_override[1], pad_rows, 0x7BFF)
     q, k, v, mask = dev(c["q"], torch), dev(kf, torch), dev(vf, torch), dev(c["mask"], torch)
     M = n_head * n_tok
     kvh_stride = (n_kv + pad_rows) * hd
@@ -48,7 +51,9 @@ def run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=0, q_f16=False, pad_
                      device="cuda")
     F.fr_decode_attn_gqa(q, F.FR_Q_F16 if q_f16 else F.FR_Q_F32, k, v, mask, out, n_inst,
                          M * hd, n_kvh * kvh_stride, 0 if mask is None else n_tok * n_kv,
-                         M * hd, n_head, n_kvh, kvh_stride, n_tok, n_kv, hd, scale, flags)
+                         M * hd, n_head, n_kvh, kvh_stride, n_tok, n_kv, hd, scale, flags,
+                         kv_len=None if kv_len is None else
+                         torch.tensor(kv_len, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -147,3 +152,96 @@ def test_gqa_workload_full_size(oracle_mod, variant):
     max_abs, rel = errors(got, want)
     print(f"[parity] {w.name} variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     assert_close(got, want, w.name)
+
+
+F16_NAN = 0x7E00
+NEG_INF = 0xFC00
+
+
+def _hide_past(c, kv_len, n_kv):
+    """The oracle's view of valid key counts: keys j >= L masked (-inf) for
+    every token; and the GPU's inputs with those K/V rows set to NaN, which
+    would poison the output if any were read."""
+    n_inst, n_tok = c["q"].shape[0], c["q"].shape[1]
+    mask = (np.zeros((n_inst, n_tok, n_kv), dtype=np.uint16) if c["mask"] is None
+            else c["mask"].copy())
+    kg, vg = c["k"].copy(), c["v"].copy()
+    for i, L in enumerate(kv_len):
+        L = min(max(L, 0), n_kv)
+        mask[i, :, L:] = NEG_INF
+        kg[i, ..., L:, :] = F16_NAN
+        vg[i, ..., L:, :] = F16_NAN
+    return dict(c, mask=mask), (kg, vg)
+
+
+KV_LEN = [  # n_head, n_kv_head, n_tok, n_kv, hd, mask kind, valid counts per instance
+    (16, 2, 5, 1000, 128, "random", [1000, 0, 1, 777, 64, 1100, -5]),
+    (8, 1, 10, 1024, 256, "none", [968, 968, 500, 1024]),
+    (32, 8, 4, 4096, 128, "zero", [4096, 2048, 33, 4000]),
+    (12, 3, 16, 333, 64, "random", [333, 320, 65, 0]),
+    (8, 2, 3, 64, 256, "zero", [64, 0, 10]),          # one key block: no split
+]
+
+
+@pytest.mark.parametrize("shape", KV_LEN, ids=lambda s: "h{}_g{}_t{}_kv{}_d{}_{}".format(*s[:6]))
+def test_device_valid_key_counts(oracle_mod, shape):
+    n_head, n_kvh, n_tok, n_kv, hd, mk, lens = shape
+    say(f"kv_len {shape}")
+    c = W.random_case(KV_LEN.index(shape) + 700, n_head, n_tok, n_kv, hd, mask_kind=mk,
+                      n_inst=len(lens), n_kv_head=n_kvh)
+    if n_kvh == 1:
+        c["k"], c["v"] = c["k"][:, None], c["v"][:, None]
+    scale = 1.0 / math.sqrt(hd)
+    c_or, kv_nan = _hide_past(c, lens, n_kv)
+    gpu_in = dict(c)
+    got = run_gqa(gpu_in, n_head, n_kvh, n_tok, n_kv, hd, scale, kv_len=lens, kv_override=kv_nan)
+    want = oracle_gqa(oracle_mod, c_or, n_head, n_kvh, n_tok, n_kv, hd, scale, oracle_mod.Q_F32)
+    max_abs, rel = errors(got, want)
+    print(f"[parity] kv_len {shape} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got, want, str(shape))
+    for i, L in enumerate(lens):
+        if L <= 0:
+            assert np.array_equal(got[i], np.zeros_like(got[i])), f"instance {i}"
+
+
+def test_graph_replays_follow_device_key_counts():
+    """One graph captured with a device key-count array; between replays the
+    host writes new counts, and every replay equals an eager call with them."""
+    import gqa_decode_attention_fr_amd as F
+    n_inst, n_head, n_kvh, n_tok, n_kv, hd = 3, 16, 4, 4, 2048, 128
+    say("graph replays with changing kv_len")
+    c = W.random_case(801, n_head, n_tok, n_kv, hd, mask_kind="none", n_inst=n_inst,
+                      n_kv_head=n_kvh)
+    scale = 1.0 / math.sqrt(hd)
+    M = n_head * n_tok
+    units, grp = n_inst * n_kvh, n_head // n_kvh
+    F.fr_decode_attn_reserve(units, grp, n_tok, n_kv, hd)
+    q, k, v = dev(c["q"], torch), dev(c["k"], torch), dev(c["v"], torch)
+    lens = torch.full((n_inst,), n_kv, dtype=torch.int32, device="cuda")
+    out = torch.zeros((n_inst, n_tok, n_head, hd), dtype=torch.float32, device="cuda")
+
+    def call():
+        F.fr_decode_attn_gqa(q, F.FR_Q_F32, k, v, None, out, n_inst, M * hd,
+                             n_kvh * n_kv * hd, 0, M * hd, n_head, n_kvh, n_kv * hd, n_tok,
+                             n_kv, hd, scale, kv_len=lens)
+
+    call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    for step, new in enumerate(([2048, 2048, 2048], [1, 100, 1999], [0, 64, 65], [513, 0, 2048])):
+        lens.copy_(torch.tensor(new, dtype=torch.int32))
+        torch.cuda.synchronize()
+        call()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {step} with counts {new}"
