@@ -67,6 +67,8 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
     p.tiles = 1;
     const int fw = env_int("FR_FORCE_WAVES", 0);   // developer knob (tests, A/B timing)
     if (fw == 4 || fw == 8) p.waves = fw;
+    // more query tokens than a 4-wave workgroup stages mask rows for
+    if (n_tok > max_tokens(p.waves)) p.waves = 8;
   }
   // Row blocks of at most waves*tiles tiles, balanced: with 5 tiles and room
   // for 4, blocks of 3 and 2 rather than 4 and 1 (the largest block sets the
@@ -133,7 +135,7 @@ int check_sizes(int n_inst, int n_head, int n_tok, int n_kv, int hd) {
   if (n_inst < 1 || n_head < 1 || n_tok < 1 || n_kv < 1 || hd < 1) return FR_ERR_INVALID;
   if (n_tok > FR_MAX_TOKENS || n_head > FR_MAX_HEADS) return FR_ERR_UNSUPPORTED;
   if (hd != 64 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
-  if (n_kv > (1 << 26)) return FR_ERR_UNSUPPORTED;
+  if (n_kv > (1 << 26) || (int64_t)n_tok * n_kv > (1 << 30)) return FR_ERR_UNSUPPORTED;
   if ((int64_t)n_inst * n_head * n_tok > (1 << 24)) return FR_ERR_UNSUPPORTED;
   return FR_OK;
 }

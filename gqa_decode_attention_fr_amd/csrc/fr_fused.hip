@@ -52,7 +52,11 @@
 namespace fr {
 namespace {
 
-enum MaskMode { kMaskNone = 0, kMaskDma = 1, kMaskReg = 2 };
+// How the mask reaches LDS: not at all (no mask), by 16-byte direct loads
+// (rows 16-byte aligned), or through registers two bytes at a time, for up to
+// 16 token rows (kMaskReg) or, in the 8-wave shape, 64 (kMaskReg64, which
+// needs four times the staging registers).
+enum MaskMode { kMaskNone = 0, kMaskDma = 1, kMaskReg = 2, kMaskReg64 = 3 };
 
 struct SplitArgs {
   const void *q;
@@ -222,7 +226,7 @@ template <int HD, int NW>
 struct Stage {
   _Float16 k[KB * HD];
   _Float16 v[KB * HD];
-  uint16_t m[NW * 64 * 8];  // one 16-byte granule per lane; 16 tokens x 8 are read
+  uint16_t m[NW * 64 * 8];  // one 16-byte granule per lane: NW*8 token rows of 64 keys
 };
 
 // NW waves per workgroup (4 or 8), TPW 16-row tiles per wave.
@@ -232,8 +236,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   constexpr int kThreads = NW * 64;
   constexpr int GPR = HD / 8;                 // 16-byte granules per K/V row
   constexpr int NJ = GPR / NW;                // K (and V) DMA instructions per wave per block
-  constexpr int NMR = (kMaxTok * KB) / kThreads; // register-path mask loads per thread
-  constexpr int NJM = MASKMODE == kMaskDma ? 1 : (MASKMODE == kMaskReg ? NMR : 0);
+  constexpr bool kReg = MASKMODE == kMaskReg || MASKMODE == kMaskReg64;
+  constexpr int kTok = MASKMODE == kMaskReg ? kMaxTok4 : max_tokens(NW); // token rows staged
+  static_assert(MASKMODE != kMaskReg64 || NW == 8, "64 register-staged rows need 8 waves");
+  static_assert(kTok * 8 <= NW * 64, "mask stage holds one granule per lane");
+  constexpr int NMR = (kTok * KB) / kThreads; // register-path mask loads per thread
+  constexpr int NJM = MASKMODE == kMaskDma ? 1 : (kReg ? NMR : 0);
   static_assert(NJ >= 1 && NJ * NW == GPR, "K/V rows split evenly over the waves");
   constexpr int J = 2 * NJ + NJM;             // vector-memory ops per wave per block
   constexpr int KS = HD / 32;
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     return;
   }
 
-  // register-staged mask values (kMaskReg only), loaded by inline assembly
+  // register-staged mask values (kMaskReg, kMaskReg64), loaded by inline assembly
   // and read only after the wait for their block
   uint32_t rm[2][NMR];
 
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     dma_vofs[j] = 2u * (uint32_t)(r * HD + 8 * (slot ^ swz_v(r, GPR)));
   }
   // mask granule of this lane: token t = lin / 8, key group (lin % 8) ^ swz_m(t);
-  // byte offset < 2^31 (n_tok <= 16, n_kv <= 2^26)
+  // byte offset < 2^31 (n_tok * n_kv <= 2^30 is checked by the host)
   const int m_lin = wave * 64 + lane;
   const int m_tok = m_lin >> 3;
   const int m_gr = (m_lin & 7) ^ swz_m(m_lin >> 3);
@@ -357,10 +365,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     if (MASKMODE == kMaskDma) {
       const bool ok = m_tok < a.n_tok && (full || kb0 + 8 * m_gr < n_eff);
       dma16((const char *)mbase, ok ? 2u * (uint32_t)kb0 + m_ofs : 0u, (char *)s.m + wave * 1024);
-    } else if (MASKMODE == kMaskReg) {
+    } else if (kReg) {
 #pragma unroll
       for (int i = 0; i < NMR; ++i) {
-        const int u = tid + i * kThreads;            // 1024 = 16 tokens x 64 keys
+        const int u = tid + i * kThreads;            // kTok tokens x 64 keys
         const int t = u >> 6, j = u & 63;
         const bool ok = t < a.n_tok && kb0 + j < n_eff;
         rmr[i] = gload_u16(mbase + (ok ? (int64_t)t * a.n_kv + kb0 + j : 0));
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       dma16(vb, dma_vofs[j] - back[j], (char *)s.v + (wave * NJ + j) * 1024);
   };
 
-  // kMaskReg: place the register-staged values (after they have arrived).
+  // kMaskReg, kMaskReg64: place the register-staged values (after they have arrived).
   // (called after the wait for the block; the empty statements keep every read
   // of the loaded registers after it)
   auto place_mask = [&](Stage<HD, NW> &s, uint32_t (&rmr)[NMR]) __attribute__((always_inline)) {
@@ -786,7 +794,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   // the prefetch; the wait for the next block is taken at the point it is
   // needed.
   for (int b = 0; b < nblk; b += 2) {
-    if (MASKMODE == kMaskReg) {
+    if (kReg) {
       place_mask(st0, rm[0]);
       wait_lgkm<0>();
     }
@@ -796,7 +804,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     if (b + 2 < nblk) issue(st0, key_begin + (b + 2) * KB, rm[0]);
     if (b + 1 >= nblk) break;
     if (b + 2 < nblk) wait_vm<J>(); else wait_vm<0>();   // block b+1 landed
-    if (MASKMODE == kMaskReg) {
+    if (kReg) {
       place_mask(st1, rm[1]);
       wait_lgkm<0>();
     }
@@ -962,6 +970,9 @@ SplitFn pick_mask(int mm) {
     case kMaskNone: return split_kernel<HD, NW, TPW, QMODE, kMaskNone>;
     case kMaskDma: return split_kernel<HD, NW, TPW, QMODE, kMaskDma>;
     case kMaskReg: return split_kernel<HD, NW, TPW, QMODE, kMaskReg>;
+    case kMaskReg64:
+      if constexpr (NW == 8) return split_kernel<HD, NW, TPW, QMODE, kMaskReg64>;
+      return nullptr;
     default: return nullptr;
   }
 }
@@ -991,7 +1002,7 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   if (p.mask) {
     const bool vec = (p.n_kv % 8 == 0) && ((uintptr_t)p.mask % 16 == 0) &&
                      (p.n_inst == 1 || p.mask_stride % 8 == 0);
-    mm = vec ? kMaskDma : kMaskReg;
+    mm = vec ? kMaskDma : (p.n_tok > kMaxTok4 ? kMaskReg64 : kMaskReg);
   }
   SplitFn fn = nullptr;
   switch (p.hd) {
@@ -999,7 +1010,8 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
     case 128: fn = pick_shape<128>(plan.waves, plan.tiles, p.qmode, mm); break;
     case 256: fn = pick_shape<256>(plan.waves, plan.tiles, p.qmode, mm); break;
   }
-  if (!fn) return hipErrorInvalidValue;
+  if (!fn || p.n_tok > max_tokens(plan.waves)) return hipErrorInvalidValue;
+  if (mm == kMaskReg && p.n_tok > kMaxTok4) return hipErrorInvalidValue;
 
   const int M = p.unit_rows();
   SplitArgs a;

@@ -10,8 +10,12 @@ namespace fr {
 
 // Keys staged through LDS per block iteration of the split kernel.
 constexpr int kKeyBlock = 64;
-// Largest query-token count (the pages' window covers q_tokens <= 16).
-constexpr int kMaxTok = 16;
+// Query tokens one split-kernel workgroup stages mask rows for: 16 (the
+// pages' window, q_tokens <= 16) in the 4-wave shape, 64 in the 8-wave shape,
+// which therefore takes every call with more than 16 tokens.
+constexpr int kMaxTok4 = 16;
+constexpr int kMaxTok8 = 64;
+constexpr int max_tokens(int waves) { return waves == 8 ? kMaxTok8 : kMaxTok4; }
 
 enum Variant { kFused = 1, kDecomposed = 2 };
 enum QMode { kQHiLo = 0, kQF16 = 1, kQRound = 2 };

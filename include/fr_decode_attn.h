@@ -75,7 +75,8 @@ extern "C" {
 typedef enum fr_status {
     FR_OK = 0,
     FR_ERR_INVALID = -1,     /* null/misaligned pointer, bad size, stride or KV-head count, out overlaps an input */
-    FR_ERR_UNSUPPORTED = -2, /* n_tok outside 1..16, hd not 64/128/256, n_head outside 1..1024 */
+    FR_ERR_UNSUPPORTED = -2, /* n_tok outside 1..64, hd not 64/128/256, n_head outside 1..1024,
+                                n_kv above 2^26 or n_tok*n_kv above 2^30 */
     FR_ERR_CAPTURE = -3,     /* the library workspace would have to grow while the stream is captured */
     FR_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
     FR_ERR_WORKSPACE = -5    /* the caller's workspace is smaller than fr_decode_attn_workspace_size */
@@ -91,7 +92,8 @@ typedef enum fr_status {
 #define FR_VARIANT_DECOMPOSED 0x4u /* force the three-launch QK^T -> softmax -> PV variant */
 
 /* Limits checked by every entry point. */
-#define FR_MAX_TOKENS 16    /* the pages' window covers q_tokens <= 16 */
+#define FR_MAX_TOKENS 64    /* the pages' window covers q_tokens <= 16; up to 64 (a
+                               speculative-verify window) are taken as well */
 #define FR_MAX_HEADS 1024
 
 /*

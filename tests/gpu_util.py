@@ -78,3 +78,46 @@ def run_gpu(case, n_head, n_tok, n_kv, hd, scale, flags=0, q_f16=False, torch=No
                             hd, scale, flags)
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def _padded_kv(x, pad_rows, fill):
+    """[n_inst, n_kvh, n_kv, hd] -> the same with pad_rows extra rows per KV
+    head holding `fill` (f16 bits), which the kernels must never read."""
+    if pad_rows == 0:
+        return x
+    n_inst, n_kvh, n_kv, hd = x.shape
+    out = np.full((n_inst, n_kvh, n_kv + pad_rows, hd), fill, dtype=np.uint16)
+    out[:, :, :n_kv] = x
+    return out
+
+
+def run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=0, q_f16=False, pad_rows=0,
+            kv_len=None, kv_override=None):
+    """fr_decode_attn_gqa on every instance of `c` (k, v as [n_inst, n_kvh, n_kv, hd])
+    in one call; returns [n_inst, n_tok, n_head, hd] float32."""
+    import torch
+    import gqa_decode_attention_fr_amd as F
+    n_inst = c["q"].shape[0]
+    kf = _padded_kv(c["k"] if kv_override is None else kv_override[0], pad_rows, 0x7BFF)
+    vf = _padded_kv(c["v"] if kv_override is None else kv_override[1], pad_rows, 0x7BFF)
+    q, k, v, mask = dev(c["q"], torch), dev(kf, torch), dev(vf, torch), dev(c["mask"], torch)
+    M = n_head * n_tok
+    kvh_stride = (n_kv + pad_rows) * hd
+    out = torch.full((n_inst, n_tok, n_head, hd), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    F.fr_decode_attn_gqa(q, F.FR_Q_F16 if q_f16 else F.FR_Q_F32, k, v, mask, out, n_inst,
+                         M * hd, n_kvh * kvh_stride, 0 if mask is None else n_tok * n_kv,
+                         M * hd, n_head, n_kvh, kvh_stride, n_tok, n_kv, hd, scale, flags,
+                         kv_len=None if kv_len is None else
+                         torch.tensor(kv_len, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_gqa(oracle, c, n_head, n_kvh, n_tok, n_kv, hd, scale, q_kind):
+    outs = []
+    for i in range(c["q"].shape[0]):
+        m = None if c["mask"] is None else c["mask"][i]
+        outs.append(oracle.decode_attn(c["q"][i], c["k"][i], c["v"][i], m, n_head, n_tok, n_kv,
+                                       hd, scale, q_kind=q_kind, n_kv_head=n_kvh))
+    return np.stack(outs)

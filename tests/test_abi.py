@@ -71,7 +71,9 @@ def call(**kw):
     (dict(n_kv=0), B.FR_ERR_INVALID),
     (dict(n_head=0), B.FR_ERR_INVALID),
     (dict(n_inst=0), B.FR_ERR_INVALID),
-    (dict(n_tok=17), B.FR_ERR_UNSUPPORTED),
+    (dict(n_tok=65), B.FR_ERR_UNSUPPORTED),
+    (dict(n_tok=64, n_kv=1 << 25), B.FR_ERR_UNSUPPORTED),  # mask offsets past 2^31 bytes
+    (dict(n_kv=(1 << 26) + 1), B.FR_ERR_UNSUPPORTED),
     (dict(hd=96), B.FR_ERR_UNSUPPORTED),
     (dict(hd=512), B.FR_ERR_UNSUPPORTED),
     (dict(n_head=1025), B.FR_ERR_UNSUPPORTED),
@@ -117,7 +119,7 @@ def gqa_call(**kw):
     (dict(kvhs=1024 * 128 + 4), B.FR_ERR_INVALID),           # breaks 16-byte alignment
     (dict(n_inst=2, os_=32 * 128, kvs=1024 * 128), B.FR_ERR_INVALID),  # instance < 2 heads
     (dict(out=K + 1024 * 128 * 2), B.FR_ERR_INVALID),        # out inside the second KV head
-    (dict(n_tok=17), B.FR_ERR_UNSUPPORTED),
+    (dict(n_tok=65), B.FR_ERR_UNSUPPORTED),
     (dict(q=None), B.FR_ERR_INVALID),
     (dict(kvl=0x600002), B.FR_ERR_INVALID),                  # misaligned key counts
     (dict(kvl=0x600000, flags=B.FR_VARIANT_DECOMPOSED), B.FR_ERR_UNSUPPORTED),
@@ -128,7 +130,7 @@ def test_gqa_rejected_before_any_launch(kw, status):
 
 def test_gqa_with_one_kv_head_validates_like_ex():
     # one KV head ignores the head stride; the rest of the checks are shared
-    for kw in (dict(n_tok=17), dict(hd=96), dict(out=Q), dict(scale=float("nan"))):
+    for kw in (dict(n_tok=65), dict(hd=96), dict(out=Q), dict(scale=float("nan"))):
         a = dict(kw)
         assert gqa_call(n_kvh=1, kvhs=-5, **a) == call(**a)
 
@@ -136,14 +138,15 @@ def test_gqa_with_one_kv_head_validates_like_ex():
 def test_single_entry_points_validate_too():
     lib = B.load()
     assert lib.fr_decode_attn(None, K, V, MASK, OUT, 8, 1, 64, 256, 0.0625, None) == B.FR_ERR_INVALID
-    assert lib.fr_decode_attn_q16(Q, K, V, MASK, OUT, 8, 17, 64, 256, 0.0625, None) == \
+    assert lib.fr_decode_attn_q16(Q, K, V, MASK, OUT, 8, 65, 64, 256, 0.0625, None) == \
         B.FR_ERR_UNSUPPORTED
     assert lib.fr_decode_attn_batched(Q, B.FR_Q_F32, K, V, MASK, OUT, 3, 0, 0, 0, 16, 8, 1, 64,
                                       256, 0.0625, None) == B.FR_ERR_INVALID
 
 
 SHAPES = [(1, 8, 1, 64, 256), (18, 8, 10, 1024, 256), (1, 16, 16, 4096, 128),
-          (1, 8, 16, 2048, 256), (1, 32, 16, 32768, 128), (3, 5, 7, 1000, 64), (1, 1, 1, 1, 64)]
+          (1, 8, 16, 2048, 256), (1, 32, 16, 32768, 128), (3, 5, 7, 1000, 64), (1, 1, 1, 1, 64),
+          (1, 8, 24, 2000, 256), (2, 4, 64, 4096, 128), (1, 1, 17, 77, 64)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -161,7 +164,8 @@ def test_plan_covers_keys_and_rows(shape, flags):
     if flags:
         assert p["waves"] == 4 and p["tiles"] == {256: 1, 128: 2, 64: 4}[hd]
     else:
-        assert p["tiles"] == 1 and p["waves"] == (4 if tiles_total <= 16 else 8)
+        # 8 waves above 16 tiles, and for more tokens than 4 waves stage mask rows for
+        assert p["tiles"] == 1 and p["waves"] == (4 if tiles_total <= 16 and n_tok <= 16 else 8)
         # one workgroup per compute unit at most, unless instances x row blocks exceed it
         assert p["grid"] <= max(256, n_inst * p["n_rowblk"])
     ws = B.fr_decode_attn_workspace_size(*shape, flags)
@@ -188,6 +192,13 @@ def test_plan_shapes(shape, want):
     assert (p["waves"], p["n_rowblk"], p["n_split"], p["chunk"]) == want
 
 
+def test_many_tokens_take_eight_waves(monkeypatch):
+    monkeypatch.setenv("FR_FORCE_WAVES", "4")
+    assert B.fr_decode_attn_plan(1, 8, 16, 1024, 256, 0)["waves"] == 4
+    assert B.fr_decode_attn_plan(1, 8, 17, 1024, 256, 0)["waves"] == 8
+    assert B.fr_decode_attn_plan(1, 2, 64, 1024, 128, 0)["waves"] == 8
+
+
 def test_forced_split_count(monkeypatch):
     monkeypatch.setenv("FR_FORCE_SPLITS", "4")
     p = B.fr_decode_attn_plan(18, 8, 10, 1024, 256, 0)
@@ -196,7 +207,7 @@ def test_forced_split_count(monkeypatch):
 
 def test_sizes_rejected_by_helpers():
     with pytest.raises(B.FrError) as e:
-        B.fr_decode_attn_workspace_size(1, 8, 17, 64, 256)
+        B.fr_decode_attn_workspace_size(1, 8, 65, 64, 256)
     assert e.value.status == B.FR_ERR_UNSUPPORTED
     info = (ctypes.c_int * 8)()
     assert B.load().fr_decode_attn_plan(1, 8, 1, 64, 96, 0, info, 8) == B.FR_ERR_UNSUPPORTED

@@ -1,0 +1,79 @@
+"""GPU parity above the pages' 16 query tokens (up to 64: a speculative-verify
+window).  Calls with more than 16 tokens run in 8-wave workgroups, which stage
+mask rows for up to 64 tokens; both mask load paths (16-byte direct loads for
+aligned rows, register staging otherwise) and both variants are checked
+against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+from gqa_decode_attention_fr_amd import workloads as W
+from gpu_util import assert_close, errors, oracle_gqa, run_gqa, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+FUSED, DECOMP = 0x2, 0x4
+NEG_INF = 0xFC00
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_decode_attention_fr_amd as F
+    F.binding.load()
+    yield
+
+
+def causal_tail_mask(n_inst, n_tok, n_kv):
+    """The last n_tok keys are the query tokens: token t sees every earlier key
+    and query keys 0..t (the verify step of speculative decoding)."""
+    m = np.zeros((n_inst, n_tok, n_kv), dtype=np.uint16)
+    base = n_kv - n_tok
+    for t in range(n_tok):
+        m[:, t, base + t + 1:] = NEG_INF
+    return m
+
+
+MANY = [  # n_inst, n_head, n_kv_head, n_tok, n_kv, hd, q dtype, mask kind
+    (1, 8, 1, 17, 1000, 256, "f32", "random"),        # 16-byte mask loads
+    (1, 8, 1, 32, 2048, 256, "f32", "causal"),
+    (2, 4, 1, 64, 4096, 128, "f32", "random"),
+    (1, 8, 1, 64, 999, 256, "f32", "random"),         # register-staged mask rows
+    (1, 16, 4, 48, 1531, 128, "f16", "random"),
+    (3, 2, 1, 33, 333, 64, "f32", "full_row"),
+    (1, 32, 8, 64, 8192, 128, "f32", "causal"),       # 256 rows per KV head
+    (2, 1, 1, 64, 65, 256, "f32", "none"),
+]
+
+
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+@pytest.mark.parametrize("shape", MANY, ids=lambda s: "n{}_h{}_g{}_t{}_kv{}_d{}_{}_{}".format(*s))
+def test_many_token_parity(oracle_mod, shape, variant):
+    n_inst, n_head, n_kvh, n_tok, n_kv, hd, qd, mk = shape
+    say(f"tokens {shape} variant={variant}")
+    c = W.random_case(MANY.index(shape) + 900, n_head, n_tok, n_kv, hd, q_dtype=qd,
+                      mask_kind="zero" if mk == "causal" else mk, n_inst=n_inst,
+                      n_kv_head=n_kvh)
+    if mk == "causal":
+        c["mask"] = causal_tail_mask(n_inst, n_tok, n_kv)
+    if n_kvh == 1:
+        c["k"], c["v"] = c["k"][:, None], c["v"][:, None]
+    scale = 1.0 / math.sqrt(hd)
+    got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=variant,
+                  q_f16=(qd == "f16"))
+    want = oracle_gqa(oracle_mod, c, n_head, n_kvh, n_tok, n_kv, hd, scale,
+                      oracle_mod.Q_F16 if qd == "f16" else oracle_mod.Q_F32)
+    max_abs, rel = errors(got, want)
+    print(f"[parity] tokens {shape} variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got, want, str(shape))
+    if mk == "full_row":
+        assert np.array_equal(got[:, 0], np.zeros_like(got[:, 0]))
+
+
+def test_sixty_four_tokens_plan_eight_waves():
+    import gqa_decode_attention_fr_amd as F
+    assert F.fr_decode_attn_plan(1, 8, 64, 999, 256)["waves"] == 8
+    assert F.fr_decode_attn_plan(1, 8, 16, 999, 256)["waves"] == 4
