@@ -282,6 +282,25 @@ def cpu_baseline(w, g, gpu_out, repeats):
             "max_abs_vs_gpu": err}
 
 
+RIDGE_FLOP_PER_BYTE = PEAK_F16_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # ~312
+
+
+def roofline(w, kern_ms, achieved_gbs, traffic):
+    """The bound of the split kernel from the workload's algorithmic intensity:
+    below the ridge it is HBM bytes per second against 8 TB/s; above it (long
+    context) the two contractions' flops against the dense f16 matrix-core
+    peak.  (An f32 query runs its score contraction twice, hi and lo; those
+    extra flops are not counted: the figure is algorithmic.)"""
+    if w.flops() / w.algorithmic_bytes() <= RIDGE_FLOP_PER_BYTE:
+        return {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic}
+    tflops = w.flops() / (kern_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_MFMA_TFLOPS, 4),
+            "traffic": traffic}
+
+
 def run_workload(args, torch, F, W, w):
     flags = {"auto": 0, "fused": F.FR_VARIANT_FUSED,
              "decomposed": F.FR_VARIANT_DECOMPOSED}[args.variant]
@@ -365,9 +384,7 @@ def run_workload(args, torch, F, W, w):
                    "n_kv_head": w.n_kv_head, "n_tok": w.n_tok, "n_kv": w.n_kv, "n_valid": w.n_valid, "hd": w.hd,
                    "q_dtype": w.q_dtype, "variant": args.variant,
                    "round_f16": bool(args.round_f16)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic},
+        "roofline": roofline(w, kern_ms, achieved, traffic),
         "aux": aux,
     }
     if not args.no_cpu_baseline:

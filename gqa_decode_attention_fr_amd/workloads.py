@@ -94,7 +94,13 @@ WORKLOADS = [TINY, PI05_ACTION_STEP, H16_HD128_Q16, CAUSAL_TAIL, LONG_CONTEXT]
 # keys, 8 independent sequences per call.
 GQA_KV8 = Workload("gqa_h32_kv8_hd128_t4_kv4096_x8", n_head=32, n_tok=4, n_kv=4096,
                    n_valid=4096, hd=128, n_inst=8, n_kv_head=8)
-EXTRA_WORKLOADS = [GQA_KV8]
+# A speculative-verify step past the pages' 16 tokens: 64 draft tokens checked
+# at once against 8192 keys, the last 64 of them the draft tokens themselves
+# (causal among them), 32 query heads on 8 KV heads.
+SPEC_VERIFY_T64 = Workload("spec_verify_h32_kv8_hd128_t64_kv8192", n_head=32, n_tok=64,
+                           n_kv=8192, n_valid=8192, hd=128, n_kv_head=8,
+                           mask_kind="causal_tail")
+EXTRA_WORKLOADS = [GQA_KV8, SPEC_VERIFY_T64]
 
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

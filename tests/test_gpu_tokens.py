@@ -77,3 +77,17 @@ def test_sixty_four_tokens_plan_eight_waves():
     import gqa_decode_attention_fr_amd as F
     assert F.fr_decode_attn_plan(1, 8, 64, 999, 256)["waves"] == 8
     assert F.fr_decode_attn_plan(1, 8, 16, 999, 256)["waves"] == 4
+
+
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+def test_spec_verify_workload_full_size(oracle_mod, variant):
+    """The measured 64-token verify workload, every element."""
+    w = W.SPEC_VERIFY_T64
+    say(f"workload {w.name} variant={variant}")
+    g = W.generate(w)
+    got = run_gqa(g, w.n_head, w.n_kv_head, w.n_tok, w.n_kv, w.hd, w.scale, flags=variant)
+    want = oracle_gqa(oracle_mod, g, w.n_head, w.n_kv_head, w.n_tok, w.n_kv, w.hd, w.scale,
+                      oracle_mod.Q_F32)
+    max_abs, rel = errors(got, want)
+    print(f"[parity] {w.name} variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got, want, w.name)

@@ -95,3 +95,12 @@ def test_several_kv_head_workload():
     assert w.algorithmic_bytes() == w.n_inst * (2 * 8 * 4096 * 128 * 2 + 128 * 128 * 4
                                                 + 4 * 4096 * 2 + 128 * 128 * 4)
     assert w.name in W.BY_NAME and w not in W.WORKLOADS
+
+
+def test_spec_verify_workload_mask():
+    w = W.SPEC_VERIFY_T64
+    m = W.build_mask(w)
+    base = w.n_kv - w.n_tok
+    assert (m[:, :base] == 0).all()
+    assert all(m[t, base + t] == 0 and (t == w.n_tok - 1 or m[t, base + t + 1] == NEG_INF)
+               for t in range(w.n_tok))
