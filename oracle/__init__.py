@@ -59,6 +59,9 @@ def _load():
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f32_to_f16_rne.restype = ctypes.c_uint16
         lib.oracle_f32_to_f16_rne.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16_rne_rows.restype = None
+        lib.oracle_f32_to_f16_rne_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_int64]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_decode_attn_f64.restype = ctypes.c_int
         lib.oracle_decode_attn_f64.argtypes = [
@@ -93,6 +96,16 @@ def f32_to_f16_rne(x) -> np.ndarray:
     flat_in, flat_out = a.reshape(-1), out.reshape(-1)
     for i in range(flat_in.size):
         flat_out[i] = lib.oracle_f32_to_f16_rne(float(flat_in[i]))
+    return out
+
+
+def f16_copy(src) -> np.ndarray:
+    """The batched f32 -> f16 row copy: every float32 rounded to binary16 bits
+    (nearest even) on its own; returns uint16 of the same shape."""
+    lib = _load()
+    a = np.ascontiguousarray(src, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib.oracle_f32_to_f16_rne_rows(a.ctypes.data, out.ctypes.data, int(a.size))
     return out
 
 

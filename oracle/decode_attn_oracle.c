@@ -93,6 +93,15 @@ uint16_t oracle_f32_to_f16_rne(float xf)
     return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)n - 1024));
 }
 
+/* A batched f32 -> f16 row copy (FlashRT PR #185, the commit batching the
+ * persistent-KV tail copies): every element rounded on its own, nearest even,
+ * exactly as one copy per row would. */
+void oracle_f32_to_f16_rne_rows(const float *src, uint16_t *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_f32_to_f16_rne(src[i]);
+}
+
 /* Element q[i] of the query tensor as fp64, for the three query kinds. */
 static double q_at(const void *q, int q_kind, size_t i)
 {

@@ -66,6 +66,17 @@ def test_f32_to_f16_rne_matches_numpy_and_stdlib(oracle_mod):
     assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0
 
 
+def test_f16_row_copy_matches_numpy_and_the_element_rounding(oracle_mod):
+    """The batched copy rounds each element on its own: numpy's nearest-even
+    cast (an independent implementation) and the element-wise oracle agree."""
+    x = _rne_test_values()
+    got = oracle_mod.f16_copy(x)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(got, x.astype(np.float16).view(np.uint16))
+    assert np.array_equal(got[:5000], oracle_mod.f32_to_f16_rne(x[:5000]))
+    assert oracle_mod.f16_copy(np.zeros(0, dtype=np.float32)).size == 0
+
+
 # --------------------------------------------------------------------------- brute force
 
 def _oracle_case(oracle_mod, c, n_head, n_tok, n_kv, hd, scale, q_kind):
