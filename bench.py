@@ -406,6 +406,58 @@ def calibrate_copy(torch, steps):
                       "bytes_written_per_copy": n * 4, "copies": max(1, steps)}), flush=True)
 
 
+COPY_WORKLOAD = "kv_tail_copy_pi05_l18_rows968_hd256"
+
+
+def run_copy_workload(args, torch, F):
+    """The batched persistent-KV tail copies after a pi0.5 prefill: per layer
+    (18) and KV tensor (K, V), the 968 prefix rows of 256 f32 -> f16, as one
+    call.  Cold inputs from a >= 1 GiB rotating pool, K plain calls behind a
+    GPU sleep; bytes = 4 read + 2 written per element."""
+    n_copy, rows, hd = 36, 968, 256
+    n = rows * hd
+    per = n_copy * n * 6
+    R = max(2, int(math.ceil(args.pool_gib * (1 << 30) / per)))
+    src = torch.randn((R, n_copy, n), dtype=torch.float32, device="cuda") * 0.5
+    dst = torch.empty((R, n_copy, n), dtype=torch.float16, device="cuda")
+    lib = F.binding.load()
+    arrs = []
+    for r in range(R):
+        arr = (F.binding.F16Copy * n_copy)()
+        for c in range(n_copy):
+            arr[c] = F.binding.F16Copy(src[r, c].data_ptr(), dst[r, c].data_ptr(), n)
+        arrs.append(arr)
+
+    def call(slot, stream):
+        st = lib.fr_f16_copy_batch(arrs[slot], n_copy, stream)
+        if st != 0:
+            raise F.FrError(st, "fr_f16_copy_batch")
+
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    for i in range(args.warmup):
+        call(i % R, stream)
+    torch.cuda.synchronize()
+    ms_call, _ = timed_region(torch, F, call, R, args.steps, stream, hook=False)
+    ms_graph = graph_region(torch, call, R, args.steps)
+    gbs = per / (ms_call * 1e-3) / 1e9
+    rec = {
+        "metric": "µs/call and achieved HBM GB/s for the batched f32->f16 KV tail copies",
+        "value": round(ms_call * 1e3, 3), "unit": "us/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_call, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32->f16",
+        "data": "synthetic (normal f32 rows)",
+        "config": {"workload": COPY_WORKLOAD, "copies": n_copy, "rows": rows, "hd": hd},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "aux": {"bytes_per_call": per, "graph_replayed_us_per_call": round(ms_graph * 1e3, 3),
+                "pool_copies": R,
+                "note": "achieved is per whole call (one launch), launch gap included"},
+    }
+    del src, dst
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -424,9 +476,12 @@ def main(argv=None):
         calibrate_copy(torch, args.steps)
         return 0
     F.binding.load()
-    names = ([w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS] if args.workload == "all"
-             else [args.workload])
+    names = ([w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS] + [COPY_WORKLOAD]
+             if args.workload == "all" else [args.workload])
     for name in names:
+        if name == COPY_WORKLOAD:
+            print(json.dumps(run_copy_workload(args, torch, F)), flush=True)
+            continue
         if name not in W.BY_NAME:
             print(f"unknown workload {name}; choose from {list(W.BY_NAME)}", file=sys.stderr)
             return 1

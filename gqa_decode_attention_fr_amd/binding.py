@@ -32,10 +32,16 @@ FR_VARIANT_DECOMPOSED = 0x4
 EXPORTED = ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
             "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_workspace_size",
             "fr_decode_attn_reserve",
-            "fr_decode_attn_plan", "fr_decode_attn_profile_events", "fr_status_str",
+            "fr_decode_attn_plan", "fr_decode_attn_profile_events", "fr_f16_copy_batch",
+            "fr_status_str",
             "fr_abi_version")
 
 PLAN_FIELDS = ("variant", "n_split", "chunk", "waves", "tiles", "n_rowblk", "grid", "launches")
+
+
+class F16Copy(ctypes.Structure):
+    """struct fr_f16_copy: n float32 at src -> binary16 bits at dst."""
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class FrError(RuntimeError):
@@ -80,6 +86,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fr_decode_attn_workspace_size.restype = sz
     lib.fr_decode_attn_reserve.argtypes = [i32, i32, i32, i32, i32, u32]
     lib.fr_decode_attn_plan.argtypes = [i32, i32, i32, i32, i32, u32, ctypes.POINTER(i32), i32]
+    lib.fr_f16_copy_batch.argtypes = [ctypes.POINTER(F16Copy), i32, vp]
+    lib.fr_f16_copy_batch.restype = i32
     lib.fr_decode_attn_profile_events.argtypes = [vp, vp]
     lib.fr_decode_attn_profile_events.restype = i32
     lib.fr_status_str.argtypes = [i32]
@@ -181,6 +189,15 @@ def fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> dict:
     _check(load().fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags, info,
                                       len(PLAN_FIELDS)), "fr_decode_attn_plan")
     return dict(zip(PLAN_FIELDS, list(info)))
+
+
+def fr_f16_copy_batch(copies, stream=None) -> None:
+    """copies: sequence of (src, dst, n) with src float32 and dst float16/uint16
+    device tensors or raw pointers; one batched f32 -> f16 conversion call."""
+    arr = (F16Copy * max(1, len(copies)))()
+    for i, (src, dst, n) in enumerate(copies):
+        arr[i] = F16Copy(_ptr(src), _ptr(dst), int(n))
+    _check(load().fr_f16_copy_batch(arr, len(copies), _stream(stream)), "fr_f16_copy_batch")
 
 
 def fr_decode_attn_profile_events(start, stop) -> None:

@@ -382,6 +382,33 @@ int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, uns
   return FR_OK;
 }
 
+int fr_f16_copy_batch(const fr_f16_copy *copies, int n_copies, void *stream) {
+  if (n_copies < 0 || n_copies > FR_MAX_COPIES || (n_copies > 0 && !copies))
+    return FR_ERR_INVALID;
+  std::vector<fr::CopyDesc> run;
+  run.reserve(n_copies);
+  std::vector<Range> src_r, dst_r;
+  for (int i = 0; i < n_copies; ++i) {
+    const fr_f16_copy &c = copies[i];
+    if (c.n < 0) return FR_ERR_INVALID;
+    if (c.n == 0) continue;
+    if (!c.src || !c.dst || !aligned(c.src, 4) || !aligned(c.dst, 2)) return FR_ERR_INVALID;
+    src_r.push_back(span(c.src, 1, 0, c.n, 4));
+    dst_r.push_back(span(c.dst, 1, 0, c.n, 2));
+    run.push_back(fr::CopyDesc{c.src, c.dst, c.n});
+  }
+  // no destination may overlap a source or another destination
+  for (size_t i = 0; i < dst_r.size(); ++i) {
+    for (size_t j = 0; j < src_r.size(); ++j)
+      if (overlaps(dst_r[i], src_r[j])) return FR_ERR_INVALID;
+    for (size_t j = i + 1; j < dst_r.size(); ++j)
+      if (overlaps(dst_r[i], dst_r[j])) return FR_ERR_INVALID;
+  }
+  if (run.empty()) return FR_OK;
+  const hipError_t err = fr::launch_f16_copies(run.data(), (int)run.size(), (hipStream_t)stream);
+  return err == hipSuccess ? FR_OK : FR_ERR_HIP;
+}
+
 int fr_decode_attn_profile_events(void *start, void *stop) {
   if ((start == nullptr) != (stop == nullptr)) return FR_ERR_INVALID;
   fr::g_prof_start.store((hipEvent_t)start);

@@ -75,6 +75,18 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
 // n_split > 1).  Returns hipSuccess or the launch error.
 hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hipStream_t stream);
 
+// One f32 -> f16 row copy of a batch (n elements, src to dst).
+struct CopyDesc {
+  const float *src;
+  uint16_t *dst;
+  int64_t n;
+};
+// Copies whose descriptors one launch carries in its kernel arguments.
+constexpr int kCopiesPerLaunch = 64;
+
+// Enqueue a run of f32 -> f16 (nearest-even) copies, kCopiesPerLaunch per launch.
+hipError_t launch_f16_copies(const CopyDesc *copies, int n_copies, hipStream_t stream);
+
 // Enqueue the three-launch decomposition: QK^T, masked softmax, PV.
 hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace,
                              hipStream_t stream);

@@ -230,6 +230,32 @@ int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd,
  */
 int fr_decode_attn_profile_events(void *start, void *stop);
 
+/*
+ * Batched f32 -> f16 row copies (the step after the window's K/V producer).
+ * FlashRT PR #185, the commit batching the persistent-KV tail copies: the
+ * prefill graph ends with one small f32 -> f16 row copy per layer and KV
+ * tensor into the persistent encoder-KV buffers, which this window then reads
+ * as K and V; a run of them is one launch, with the same rounding per element.
+ *
+ * Copy i converts copies[i].n float32 values at copies[i].src to IEEE binary16
+ * bits at copies[i].dst, rounding to nearest, ties to even (magnitudes from
+ * 65520 up become infinity; NaN inputs give an unspecified NaN).  `copies` is
+ * a HOST array of n_copies descriptors (0 <= n_copies <= FR_MAX_COPIES), read
+ * during the call only; src and dst are DEVICE pointers (src 4-byte, dst
+ * 2-byte aligned; 16-byte alignment of both takes the vector path).  No
+ * destination may overlap a source or another destination (FR_ERR_INVALID).
+ * Copies with n = 0 are skipped.  Up to 64 copies go in one launch, their
+ * descriptors in the kernel arguments, so the call is capture-safe.
+ * Returns FR_OK or a negative fr_status.
+ */
+typedef struct fr_f16_copy {
+    const float *src;
+    uint16_t *dst;
+    int64_t n;
+} fr_f16_copy;
+#define FR_MAX_COPIES 4096
+int fr_f16_copy_batch(const fr_f16_copy *copies, int n_copies, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *fr_status_str(int status);
 

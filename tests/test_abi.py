@@ -211,3 +211,32 @@ def test_sizes_rejected_by_helpers():
     assert e.value.status == B.FR_ERR_UNSUPPORTED
     info = (ctypes.c_int * 8)()
     assert B.load().fr_decode_attn_plan(1, 8, 1, 64, 96, 0, info, 8) == B.FR_ERR_UNSUPPORTED
+
+
+def copy_call(entries, n=None):
+    arr = (B.F16Copy * max(1, len(entries)))()
+    for i, (s, d, cnt) in enumerate(entries):
+        arr[i] = B.F16Copy(s, d, cnt)
+    return B.load().fr_f16_copy_batch(arr, len(entries) if n is None else n, None)
+
+
+@pytest.mark.parametrize("entries,n,status", [
+    ([], -1, B.FR_ERR_INVALID),
+    ([(Q, K, 16)], 4097, B.FR_ERR_INVALID),                 # above FR_MAX_COPIES
+    ([(Q, K, -1)], None, B.FR_ERR_INVALID),
+    ([(None, K, 16)], None, B.FR_ERR_INVALID),
+    ([(Q, None, 16)], None, B.FR_ERR_INVALID),
+    ([(Q + 2, K, 16)], None, B.FR_ERR_INVALID),             # src not 4-byte aligned
+    ([(Q, K + 1, 16)], None, B.FR_ERR_INVALID),             # dst not 2-byte aligned
+    ([(Q, Q + 8, 16)], None, B.FR_ERR_INVALID),             # dst overlaps its source
+    ([(Q, K, 16), (V, K + 16, 16)], None, B.FR_ERR_INVALID),  # two destinations overlap
+    ([(Q, K, 16), (V, Q + 60, 16)], None, B.FR_ERR_INVALID),  # dst over another source
+    ([], 0, B.FR_OK),                                        # nothing to do, no launch
+    ([(None, None, 0), (Q, None, 0)], None, B.FR_OK),        # empty copies are skipped
+])
+def test_copy_batch_validation(entries, n, status):
+    assert copy_call(entries, n) == status
+
+
+def test_copy_batch_null_array():
+    assert B.load().fr_f16_copy_batch(None, 3, None) == B.FR_ERR_INVALID
