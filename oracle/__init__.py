@@ -62,6 +62,11 @@ def _load():
         lib.oracle_f32_to_f16_rne_rows.restype = None
         lib.oracle_f32_to_f16_rne_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                                     ctypes.c_int64]
+        lib.oracle_qkv_post_f64.restype = None
+        lib.oracle_qkv_post_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_decode_attn_f64.restype = ctypes.c_int
         lib.oracle_decode_attn_f64.argtypes = [
@@ -107,6 +112,28 @@ def f16_copy(src) -> np.ndarray:
     out = np.empty(a.shape, dtype=np.uint16)
     lib.oracle_f32_to_f16_rne_rows(a.ctypes.data, out.ctypes.data, int(a.size))
     return out
+
+
+def qkv_post(qkv, pos, n_head: int, n_kv_head: int, n_tok: int, hd: int, base: float,
+             q_scale: float):
+    """RoPE (NeoX form) and the query scale applied to one instance's fused QKV
+    projection output, in fp64.
+
+    qkv : [n_tok, (n_head + 2*n_kv_head) * hd] float32;  pos : [n_tok] int
+    returns q [n_tok, n_head, hd], k [n_kv_head, n_tok, hd], v [n_kv_head, n_tok, hd]
+    """
+    lib = _load()
+    a = np.ascontiguousarray(qkv, dtype=np.float32)
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    if a.size != n_tok * (n_head + 2 * n_kv_head) * hd or p.size != n_tok or hd % 2:
+        raise ValueError("oracle: qkv_post sizes do not match")
+    q = np.empty((n_tok, n_head, hd), dtype=np.float64)
+    k = np.empty((n_kv_head, n_tok, hd), dtype=np.float64)
+    v = np.empty((n_kv_head, n_tok, hd), dtype=np.float64)
+    lib.oracle_qkv_post_f64(a.ctypes.data, p.ctypes.data, int(n_head), int(n_kv_head),
+                            int(n_tok), int(hd), float(base), float(q_scale), q.ctypes.data,
+                            k.ctypes.data, v.ctypes.data)
+    return q, k, v
 
 
 def max_threads() -> int:

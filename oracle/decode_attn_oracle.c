@@ -102,6 +102,54 @@ void oracle_f32_to_f16_rne_rows(const float *src, uint16_t *dst, int64_t n)
         dst[i] = oracle_f32_to_f16_rne(src[i]);
 }
 
+/*
+ * The query/KV producer ahead of the window (FlashRT PR #185: the prefix QKV
+ * window fuses the q/k/v projections' epilogue -- RoPE, the query scale and
+ * the f16 materialisations -- into "qkv_post", whose f16 Q rows in t-major
+ * order are what the decode window reads).  RoPE in its NeoX form, written
+ * from its definition: head vector x (length hd), position p, for i < hd/2
+ *     a_i      = p * base^(-2i/hd)
+ *     y_i      = x_i cos a_i - x_{i+hd/2} sin a_i
+ *     y_{i+hd/2} = x_{i+hd/2} cos a_i + x_i sin a_i
+ * qkv  : [n_tok][(n_head + 2*n_kv_head) * hd] f32 (query heads, key heads,
+ *        value heads of each token)
+ * pos  : [n_tok] positions
+ * q    : [n_tok][n_head][hd]      rope(q) * q_scale       (fp64)
+ * k, v : [n_kv_head][n_tok][hd]   rope(k), v unchanged    (fp64)
+ */
+void oracle_qkv_post_f64(const float *qkv, const int32_t *pos, int n_head, int n_kv_head,
+                         int n_tok, int hd, double base, double q_scale,
+                         double *q, double *k, double *v)
+{
+    const int half = hd / 2;
+    const int width = (n_head + 2 * n_kv_head) * hd;
+    for (int t = 0; t < n_tok; ++t) {
+        const float *row = qkv + (size_t)t * width;
+        for (int h = 0; h < n_head + 2 * n_kv_head; ++h) {
+            const float *x = row + (size_t)h * hd;
+            double *y;
+            if (h < n_head)
+                y = q + ((size_t)t * n_head + h) * hd;
+            else if (h < n_head + n_kv_head)
+                y = k + ((size_t)(h - n_head) * n_tok + t) * hd;
+            else
+                y = v + ((size_t)(h - n_head - n_kv_head) * n_tok + t) * hd;
+            if (h >= n_head + n_kv_head) { /* values: no rotation */
+                for (int d = 0; d < hd; ++d)
+                    y[d] = (double)x[d];
+                continue;
+            }
+            const double s = h < n_head ? q_scale : 1.0;
+            for (int i = 0; i < half; ++i) {
+                const double a = (double)pos[t] * pow(base, -2.0 * i / hd);
+                const double c = cos(a), sn = sin(a);
+                y[i] = ((double)x[i] * c - (double)x[i + half] * sn) * s;
+                y[i + half] = ((double)x[i + half] * c + (double)x[i] * sn) * s;
+            }
+        }
+    }
+}
+
 /* Element q[i] of the query tensor as fp64, for the three query kinds. */
 static double q_at(const void *q, int q_kind, size_t i)
 {

@@ -385,3 +385,58 @@ def test_matches_torch_sdpa_float64(oracle_mod, seed):
     ref = ref.permute(1, 0, 2).numpy()
     finite = np.isfinite(ref).all(axis=(1, 2))
     np.testing.assert_allclose(out[finite], ref[finite], rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- qkv_post (RoPE)
+
+def _qkv_case(seed, n_head, n_kvh, n_tok, hd):
+    rng = np.random.default_rng(seed)
+    qkv = rng.standard_normal((n_tok, (n_head + 2 * n_kvh) * hd)).astype(np.float32)
+    pos = rng.integers(0, 5000, n_tok).astype(np.int32)
+    return qkv, pos
+
+
+def test_rope_matches_complex_rotation(oracle_mod):
+    """NeoX RoPE is pair (i, i + hd/2) as one complex number times
+    exp(i * p * base^(-2i/hd)): numpy's complex arithmetic, not the oracle's
+    cos/sin expansion.  A wrong sign, pairing or frequency fails here."""
+    n_head, n_kvh, n_tok, hd, base, s = 3, 1, 4, 16, 10000.0, 0.37
+    qkv, pos = _qkv_case(11, n_head, n_kvh, n_tok, hd)
+    q, k, v = oracle_mod.qkv_post(qkv, pos, n_head, n_kvh, n_tok, hd, base, s)
+    half = hd // 2
+    freq = base ** (-2.0 * np.arange(half) / hd)
+    x = qkv.astype(np.float64).reshape(n_tok, n_head + 2 * n_kvh, hd)
+    rot = np.exp(1j * pos[:, None, None].astype(np.float64) * freq[None, None, :])
+    zq = (x[:, :n_head, :half] + 1j * x[:, :n_head, half:]) * rot * s
+    zk = (x[:, n_head:n_head + n_kvh, :half] + 1j * x[:, n_head:n_head + n_kvh, half:]) * rot
+    np.testing.assert_allclose(q, np.concatenate([zq.real, zq.imag], -1), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k, np.concatenate([zk.real, zk.imag], -1).transpose(1, 0, 2),
+                               rtol=0, atol=1e-12)
+    assert np.array_equal(v, x[:, n_head + n_kvh:, :].transpose(1, 0, 2))
+
+
+def test_rope_position_zero_is_identity(oracle_mod):
+    n_head, n_kvh, n_tok, hd = 4, 2, 3, 8
+    qkv, _ = _qkv_case(12, n_head, n_kvh, n_tok, hd)
+    q, k, v = oracle_mod.qkv_post(qkv, np.zeros(n_tok, np.int32), n_head, n_kvh, n_tok, hd,
+                                  10000.0, 0.5)
+    x = qkv.astype(np.float64).reshape(n_tok, n_head + 2 * n_kvh, hd)
+    assert np.array_equal(q, x[:, :n_head] * 0.5)
+    assert np.array_equal(k, x[:, n_head:n_head + n_kvh].transpose(1, 0, 2))
+
+
+def test_rope_scores_depend_only_on_relative_position(oracle_mod):
+    """<rope(q, m), rope(k, n)> is a function of m - n: shifting both
+    positions leaves every query-key score unchanged."""
+    n_head, n_kvh, n_tok, hd = 2, 1, 5, 32
+    qkv, pos = _qkv_case(13, n_head, n_kvh, n_tok, hd)
+    q0, k0, _ = oracle_mod.qkv_post(qkv, pos, n_head, n_kvh, n_tok, hd, 10000.0, 1.0)
+    q1, k1, _ = oracle_mod.qkv_post(qkv, pos + 777, n_head, n_kvh, n_tok, hd, 10000.0, 1.0)
+    s0 = np.einsum("thd,usd->thus", q0, k0.transpose(1, 0, 2))
+    s1 = np.einsum("thd,usd->thus", q1, k1.transpose(1, 0, 2))
+    np.testing.assert_allclose(s0, s1, rtol=0, atol=1e-9)
+    # and each rotated pair keeps its length
+    x = qkv.astype(np.float64).reshape(n_tok, n_head + 2 * n_kvh, hd)[:, :n_head]
+    h = hd // 2
+    np.testing.assert_allclose(q0[..., :h] ** 2 + q0[..., h:] ** 2,
+                               x[..., :h] ** 2 + x[..., h:] ** 2, rtol=1e-12)
