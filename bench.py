@@ -458,6 +458,61 @@ def run_copy_workload(args, torch, F):
     return rec
 
 
+QKV_WORKLOAD = "qkv_post_pi05_l18_h8_hd256_t10"
+
+
+def run_qkv_workload(args, torch, F):
+    """The producer ahead of the window for one pi0.5 action step: 18 layers
+    (instances) of 10 tokens, 8 query heads and 1 KV head of 256, RoPE base
+    10000, K/V rows stored into 1024-row caches.  Cold inputs from a rotating
+    pool; bytes = qkv read + positions + f16 query, key and value rows."""
+    n_inst, n_tok, n_head, n_kvh, hd, cap = 18, 10, 8, 1, 256, 1024
+    width = (n_head + 2 * n_kvh) * hd
+    per_in = n_inst * n_tok * (width * 4 + 4)
+    per_out = n_inst * n_tok * (n_head + 2 * n_kvh) * hd * 2
+    per = per_in + per_out
+    R = max(2, int(math.ceil(args.pool_gib * (1 << 30) / (per_in + n_inst * 2 * cap * hd * 2))))
+    qkv = torch.randn((R, n_inst, n_tok, width), dtype=torch.float32, device="cuda")
+    pos = (torch.arange(n_tok, dtype=torch.int32, device="cuda") + 958).repeat(R, n_inst, 1)
+    q16 = torch.empty((R, n_inst, n_tok, n_head, hd), dtype=torch.float16, device="cuda")
+    kc = torch.zeros((R, n_inst, n_kvh, cap, hd), dtype=torch.float16, device="cuda")
+    vc = torch.zeros_like(kc)
+    lib = F.binding.load()
+
+    def call(slot, stream):
+        st = lib.fr_qkv_post(qkv[slot].data_ptr(), pos[slot].data_ptr(), q16[slot].data_ptr(),
+                             kc[slot].data_ptr(), vc[slot].data_ptr(), n_inst, n_tok * width,
+                             n_tok, n_tok * n_head * hd, n_kvh * cap * hd, cap * hd, n_head,
+                             n_kvh, n_tok, hd, cap, 10000.0, 1.0, stream)
+        if st != 0:
+            raise F.FrError(st, "fr_qkv_post")
+
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    for i in range(args.warmup):
+        call(i % R, stream)
+    torch.cuda.synchronize()
+    ms_call, _ = timed_region(torch, F, call, R, args.steps, stream, hook=False)
+    ms_graph = graph_region(torch, call, R, args.steps)
+    gbs = per / (ms_call * 1e-3) / 1e9
+    rec = {
+        "metric": "µs/call and achieved HBM GB/s for the query/KV producer (RoPE, f16 rows)",
+        "value": round(ms_call * 1e3, 3), "unit": "us/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_call, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 -> f16 (angles f64)", "data": "synthetic (normal f32 projections)",
+        "config": {"workload": QKV_WORKLOAD, "n_inst": n_inst, "n_tok": n_tok,
+                   "n_head": n_head, "n_kv_head": n_kvh, "hd": hd},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "aux": {"bytes_per_call": per, "graph_replayed_us_per_call": round(ms_graph * 1e3, 3),
+                "pool_copies": R,
+                "note": "one launch of 180 workgroups; the call is launch-latency bound"},
+    }
+    del qkv, pos, q16, kc, vc
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -476,11 +531,14 @@ def main(argv=None):
         calibrate_copy(torch, args.steps)
         return 0
     F.binding.load()
-    names = ([w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS] + [COPY_WORKLOAD]
+    names = ([w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS] + [COPY_WORKLOAD, QKV_WORKLOAD]
              if args.workload == "all" else [args.workload])
     for name in names:
         if name == COPY_WORKLOAD:
             print(json.dumps(run_copy_workload(args, torch, F)), flush=True)
+            continue
+        if name == QKV_WORKLOAD:
+            print(json.dumps(run_qkv_workload(args, torch, F)), flush=True)
             continue
         if name not in W.BY_NAME:
             print(f"unknown workload {name}; choose from {list(W.BY_NAME)}", file=sys.stderr)

@@ -33,6 +33,7 @@ EXPORTED = ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
             "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_workspace_size",
             "fr_decode_attn_reserve",
             "fr_decode_attn_plan", "fr_decode_attn_profile_events", "fr_f16_copy_batch",
+            "fr_qkv_post",
             "fr_status_str",
             "fr_abi_version")
 
@@ -86,6 +87,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fr_decode_attn_workspace_size.restype = sz
     lib.fr_decode_attn_reserve.argtypes = [i32, i32, i32, i32, i32, u32]
     lib.fr_decode_attn_plan.argtypes = [i32, i32, i32, i32, i32, u32, ctypes.POINTER(i32), i32]
+    lib.fr_qkv_post.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32,
+                                i32, i32, i32, f32, f32, vp]
+    lib.fr_qkv_post.restype = i32
     lib.fr_f16_copy_batch.argtypes = [ctypes.POINTER(F16Copy), i32, vp]
     lib.fr_f16_copy_batch.restype = i32
     lib.fr_decode_attn_profile_events.argtypes = [vp, vp]
@@ -189,6 +193,16 @@ def fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> dict:
     _check(load().fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags, info,
                                       len(PLAN_FIELDS)), "fr_decode_attn_plan")
     return dict(zip(PLAN_FIELDS, list(info)))
+
+
+def fr_qkv_post(qkv, pos, q16, k_cache, v_cache, n_inst, qkv_stride, pos_stride, q16_stride,
+                cache_stride, cache_head_stride, n_head, n_kv_head, n_tok, hd, capacity,
+                rope_base, q_scale, stream=None) -> None:
+    """RoPE + query scale + f16 rows: q16 for the window, K/V into the caches."""
+    _check(load().fr_qkv_post(_ptr(qkv), _ptr(pos), _ptr(q16), _ptr(k_cache), _ptr(v_cache),
+                              n_inst, qkv_stride, pos_stride, q16_stride, cache_stride,
+                              cache_head_stride, n_head, n_kv_head, n_tok, hd, capacity,
+                              rope_base, q_scale, _stream(stream)), "fr_qkv_post")
 
 
 def fr_f16_copy_batch(copies, stream=None) -> None:

@@ -382,6 +382,68 @@ int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, uns
   return FR_OK;
 }
 
+int fr_qkv_post(const float *qkv, const int32_t *pos, uint16_t *q16, uint16_t *k_cache,
+                uint16_t *v_cache, int n_inst, int64_t qkv_stride, int64_t pos_stride,
+                int64_t q16_stride, int64_t cache_stride, int64_t cache_head_stride,
+                int n_head, int n_kv_head, int n_tok, int hd, int capacity, float rope_base,
+                float q_scale, void *stream) {
+  if (!qkv || !pos || !q16 || (!k_cache) != (!v_cache)) return FR_ERR_INVALID;
+  if (n_inst < 1 || n_head < 1 || n_kv_head < 1 || n_tok < 1) return FR_ERR_INVALID;
+  if (n_tok > FR_MAX_TOKENS || n_head > FR_MAX_HEADS || n_kv_head > FR_MAX_HEADS)
+    return FR_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
+  if (!std::isfinite(rope_base) || !(rope_base > 0.f) || !std::isfinite(q_scale))
+    return FR_ERR_INVALID;
+  if (!aligned(qkv, 4) || !aligned(pos, 4) || !aligned(q16, 2)) return FR_ERR_INVALID;
+  const int64_t width = (int64_t)(n_head + 2 * n_kv_head) * hd;
+  const int64_t qkv_elems = (int64_t)n_tok * width, q_elems = (int64_t)n_tok * n_head * hd;
+  int64_t cache_elems = 0;
+  if (k_cache) {
+    if (!aligned(k_cache, 2) || !aligned(v_cache, 2) || capacity < 1) return FR_ERR_INVALID;
+    if (n_kv_head > 1 && cache_head_stride < (int64_t)capacity * hd) return FR_ERR_INVALID;
+    cache_elems = (int64_t)(n_kv_head - 1) * (n_kv_head > 1 ? cache_head_stride : 0) +
+                  (int64_t)capacity * hd;
+  }
+  if (n_inst > 1) {
+    if (qkv_stride < qkv_elems || q16_stride < q_elems) return FR_ERR_INVALID;
+    if (pos_stride < 0 || (pos_stride != 0 && pos_stride < n_tok)) return FR_ERR_INVALID;
+    if (k_cache && cache_stride < cache_elems) return FR_ERR_INVALID;
+  } else {
+    qkv_stride = pos_stride = q16_stride = cache_stride = 0;
+  }
+  if (n_kv_head == 1) cache_head_stride = 0;
+  const Range rq = span(q16, n_inst, q16_stride, q_elems, 2);
+  const Range rin = span(qkv, n_inst, qkv_stride, qkv_elems, 4);
+  const Range rpos = span(pos, n_inst, pos_stride, n_tok, 4);
+  if (overlaps(rq, rin) || overlaps(rq, rpos)) return FR_ERR_INVALID;
+  if (k_cache) {
+    const Range rk = span(k_cache, n_inst, cache_stride, cache_elems, 2);
+    const Range rv = span(v_cache, n_inst, cache_stride, cache_elems, 2);
+    if (overlaps(rk, rv) || overlaps(rk, rq) || overlaps(rv, rq) || overlaps(rk, rin) ||
+        overlaps(rv, rin) || overlaps(rk, rpos) || overlaps(rv, rpos))
+      return FR_ERR_INVALID;
+  }
+  fr::QkvPostArgs a;
+  a.qkv = qkv;
+  a.pos = pos;
+  a.q16 = q16;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.qkv_stride = qkv_stride;
+  a.pos_stride = pos_stride;
+  a.q16_stride = q16_stride;
+  a.cache_stride = cache_stride;
+  a.cache_head_stride = cache_head_stride;
+  a.n_head = n_head;
+  a.n_kvh = n_kv_head;
+  a.hd = hd;
+  a.capacity = capacity;
+  a.log2_base = std::log2((double)rope_base);
+  a.q_scale = q_scale;
+  const hipError_t err = fr::launch_qkv_post(a, n_tok, n_inst, (hipStream_t)stream);
+  return err == hipSuccess ? FR_OK : FR_ERR_HIP;
+}
+
 int fr_f16_copy_batch(const fr_f16_copy *copies, int n_copies, void *stream) {
   if (n_copies < 0 || n_copies > FR_MAX_COPIES || (n_copies > 0 && !copies))
     return FR_ERR_INVALID;

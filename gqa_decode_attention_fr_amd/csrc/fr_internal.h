@@ -87,6 +87,20 @@ constexpr int kCopiesPerLaunch = 64;
 // Enqueue a run of f32 -> f16 (nearest-even) copies, kCopiesPerLaunch per launch.
 hipError_t launch_f16_copies(const CopyDesc *copies, int n_copies, hipStream_t stream);
 
+// The query/KV producer (RoPE, query scale, f16 rows).  Strides in elements.
+struct QkvPostArgs {
+  const float *qkv;       // [n_inst][n_tok][(n_head + 2*n_kvh) * hd]
+  const int32_t *pos;     // [n_inst][n_tok] positions
+  uint16_t *q16;          // [n_inst][n_tok][n_head][hd]
+  uint16_t *k_cache;      // [n_inst][n_kvh][capacity][hd], or null (no K/V store)
+  uint16_t *v_cache;
+  int64_t qkv_stride, pos_stride, q16_stride, cache_stride, cache_head_stride;
+  int n_head, n_kvh, hd, capacity;
+  double log2_base;       // log2 of the RoPE base
+  float q_scale;
+};
+hipError_t launch_qkv_post(const QkvPostArgs &a, int n_tok, int n_inst, hipStream_t stream);
+
 // Enqueue the three-launch decomposition: QK^T, masked softmax, PV.
 hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace,
                              hipStream_t stream);

@@ -231,6 +231,43 @@ int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd,
 int fr_decode_attn_profile_events(void *start, void *stop);
 
 /*
+ * The step before the window: the query/KV producer ("qkv_post").  FlashRT
+ * PR #185 folds the epilogue of the q/k/v projections -- RoPE, the query
+ * scale and the f16 materialisations -- into one pass, and its qkv_post
+ * handoff commit stores the rope'd, scaled query rows as f16 in exactly the
+ * t-major order this window reads (fr_decode_attn_q16 / FR_Q_F16), so no
+ * gather runs.  Per instance, token t (position pos[t]) and head:
+ *
+ *   RoPE, NeoX form: for i < hd/2 the pair (x_i, x_{i+hd/2}) is rotated by
+ *   a_i = pos * rope_base^(-2i/hd):  y_i = x_i cos a_i - x_{i+hd/2} sin a_i,
+ *   y_{i+hd/2} = x_{i+hd/2} cos a_i + x_i sin a_i.
+ *   q16[t][h]           = f16(rope(q) * q_scale)           (query heads)
+ *   k_cache[kh][pos[t]] = f16(rope(k)), v_cache[kh][pos[t]] = f16(v)
+ *
+ * qkv   float32 [n_tok][(n_head + 2*n_kv_head) * hd]: each token's query
+ *       heads, then key heads, then value heads (a fused QKV projection row).
+ * pos   DEVICE int32 [n_tok] positions (read when the kernel runs, so a
+ *       captured graph replays with the current values).
+ * q16   binary16 bits [n_tok][n_head][hd].
+ * k_cache, v_cache  binary16 bits [n_kv_head][capacity][hd], KV head kh at
+ *       + kh*cache_head_stride (>= capacity*hd when n_kv_head > 1); both NULL
+ *       to produce q16 only.  Token t's key and value rows go to row pos[t];
+ *       positions outside [0, capacity) are not stored.
+ * Instance i reads qkv + i*qkv_stride and pos + i*pos_stride (0: shared) and
+ * writes q16 + i*q16_stride and the caches + i*cache_stride (ELEMENTS).
+ * hd is 64, 128 or 256; 1 <= n_tok <= FR_MAX_TOKENS; rope_base > 0.
+ * Angles are computed in double precision, the rotations in fp32, each output
+ * rounded to f16 nearest-even.  No output may overlap an input or another
+ * output.  Returns FR_OK or a negative fr_status.
+ */
+int fr_qkv_post(const float *qkv, const int32_t *pos, uint16_t *q16,
+                uint16_t *k_cache, uint16_t *v_cache, int n_inst,
+                int64_t qkv_stride, int64_t pos_stride, int64_t q16_stride,
+                int64_t cache_stride, int64_t cache_head_stride, int n_head,
+                int n_kv_head, int n_tok, int hd, int capacity, float rope_base,
+                float q_scale, void *stream);
+
+/*
  * Batched f32 -> f16 row copies (the step after the window's K/V producer).
  * FlashRT PR #185, the commit batching the persistent-KV tail copies: the
  * prefill graph ends with one small f32 -> f16 row copy per layer and KV

@@ -240,3 +240,33 @@ def test_copy_batch_validation(entries, n, status):
 
 def test_copy_batch_null_array():
     assert B.load().fr_f16_copy_batch(None, 3, None) == B.FR_ERR_INVALID
+
+
+def qkv_call(**kw):
+    a = dict(qkv=Q, pos=MASK, q16=OUT, kc=K, vc=V, n_inst=1, qs=0, ps=0, q16s=0, cs=0,
+             chs=0, n_head=8, n_kvh=1, n_tok=10, hd=256, cap=1024, base=10000.0, qscale=0.0625)
+    a.update(kw)
+    return B.load().fr_qkv_post(a["qkv"], a["pos"], a["q16"], a["kc"], a["vc"], a["n_inst"],
+                                a["qs"], a["ps"], a["q16s"], a["cs"], a["chs"], a["n_head"],
+                                a["n_kvh"], a["n_tok"], a["hd"], a["cap"], a["base"],
+                                a["qscale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=None), B.FR_ERR_INVALID),
+    (dict(pos=None), B.FR_ERR_INVALID),
+    (dict(q16=None), B.FR_ERR_INVALID),
+    (dict(vc=None), B.FR_ERR_INVALID),                      # K cache without V cache
+    (dict(hd=96), B.FR_ERR_UNSUPPORTED),
+    (dict(n_tok=65), B.FR_ERR_UNSUPPORTED),
+    (dict(base=0.0), B.FR_ERR_INVALID),
+    (dict(base=float("inf")), B.FR_ERR_INVALID),
+    (dict(qscale=float("nan")), B.FR_ERR_INVALID),
+    (dict(cap=0), B.FR_ERR_INVALID),
+    (dict(n_kvh=2, chs=100), B.FR_ERR_INVALID),              # KV heads would overlap
+    (dict(n_inst=2, qs=10, q16s=8 * 10 * 256, cs=1 << 20), B.FR_ERR_INVALID),
+    (dict(q16=Q + 64), B.FR_ERR_INVALID),                    # q16 overlaps qkv
+    (dict(kc=OUT + 4096), B.FR_ERR_INVALID),                 # K cache overlaps q16
+])
+def test_qkv_post_rejected_before_any_launch(kw, status):
+    assert qkv_call(**kw) == status
