@@ -108,18 +108,27 @@ def make_call(F, w, pool, flags):
     ptrs = [(pool.q[r].data_ptr(), pool.k[r].data_ptr(), pool.v[r].data_ptr(),
              pool.mask[r].data_ptr(), pool.out[r].data_ptr()) for r in range(pool.R)]
 
+    kv_len = None
+    if w.dynamic_len:   # valid keys as device counts, one per instance
+        import torch
+        kv_len = torch.full((w.n_inst,), w.n_valid, dtype=torch.int32, device="cuda")
+    kv_len_ptr = None if kv_len is None else kv_len.data_ptr()
+
     def call(slot, stream):
         q, k, v, m, o = ptrs[slot]
-        if w.n_kv_head == 1:
+        if w.mask_kind == "none":
+            m = None
+        if w.n_kv_head == 1 and kv_len is None:
             st = lib.fr_decode_attn_ex(q, fmt, k, v, m, o, w.n_inst, qs, ks, ms, os_, w.n_head,
                                        w.n_tok, w.n_kv, w.hd, w.scale, flags, None, 0, stream)
         else:
-            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, None, o, w.n_inst, qs, ks, ms, os_,
+            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, kv_len_ptr, o, w.n_inst, qs, ks, ms, os_,
                                         w.n_head, w.n_kv_head, kvh_stride, w.n_tok, w.n_kv,
                                         w.hd, w.scale, flags, None, 0, stream)
         if st != 0:
             raise F.FrError(st, "decode attention call")
 
+    call.keep = kv_len   # the device counts live as long as the call
     return call
 
 
@@ -134,17 +143,25 @@ def make_single_calls(F, w, pool, flags):
              w.n_tok * w.n_kv * 2, M * w.hd * 4)
     ptrs = [(pool.q[r].data_ptr(), pool.k[r].data_ptr(), pool.v[r].data_ptr(),
              pool.mask[r].data_ptr(), pool.out[r].data_ptr()) for r in range(pool.R)]
+    kv_len = None
+    if w.dynamic_len:
+        import torch
+        kv_len = torch.full((1,), w.n_valid, dtype=torch.int32, device="cuda")
+    kv_len_ptr = None if kv_len is None else kv_len.data_ptr()
 
     def call(slot, stream):
         base = ptrs[slot]
         for i in range(w.n_inst):
             q, k, v, m, o = (b + i * d for b, d in zip(base, steps))
-            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, None, o, 1, 0, 0, 0, 0, w.n_head,
+            if w.mask_kind == "none":
+                m = None
+            st = lib.fr_decode_attn_gqa(q, fmt, k, v, m, kv_len_ptr, o, 1, 0, 0, 0, 0, w.n_head,
                                         w.n_kv_head, kvh_stride, w.n_tok, w.n_kv, w.hd,
                                         w.scale, flags, None, 0, stream)
             if st != 0:
                 raise F.FrError(st, "fr_decode_attn_gqa")
 
+    call.keep = kv_len
     return call
 
 
@@ -266,10 +283,16 @@ def cpu_baseline(w, g, gpu_out, repeats):
         t = time.perf_counter()
         res = []
         for i in range(w.n_inst):
-            o, threads = oracle.decode_attn(g["q"][i], g["k"][i], g["v"][i], g["mask"][i],
-                                            w.n_head, w.n_tok, w.n_kv, w.hd, w.scale,
-                                            q_kind=q_kind, return_threads=True,
-                                            n_kv_head=w.n_kv_head)
+            if w.mask_kind == "none":   # no mask; the valid keys only
+                k, v = g["k"][i][..., :w.n_valid, :], g["v"][i][..., :w.n_valid, :]
+                o, threads = oracle.decode_attn(g["q"][i], k, v, None, w.n_head, w.n_tok,
+                                                w.n_valid, w.hd, w.scale, q_kind=q_kind,
+                                                return_threads=True, n_kv_head=w.n_kv_head)
+            else:
+                o, threads = oracle.decode_attn(g["q"][i], g["k"][i], g["v"][i], g["mask"][i],
+                                                w.n_head, w.n_tok, w.n_kv, w.hd, w.scale,
+                                                q_kind=q_kind, return_threads=True,
+                                                n_kv_head=w.n_kv_head)
             res.append(o)
         times.append(time.perf_counter() - t)
         out = np.stack(res)

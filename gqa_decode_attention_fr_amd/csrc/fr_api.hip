@@ -68,7 +68,7 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
     const int fw = env_int("FR_FORCE_WAVES", 0);   // developer knob (tests, A/B timing)
     if (fw == 4 || fw == 8) p.waves = fw;
     // more query tokens than a 4-wave workgroup stages mask rows for
-    if (n_tok > max_tokens(p.waves)) p.waves = 8;
+    if (n_tok > max_tokens(4)) p.waves = 8;
   }
   // Row blocks of at most waves*tiles tiles, balanced: with 5 tiles and room
   // for 4, blocks of 3 and 2 rather than 4 and 1 (the largest block sets the
@@ -131,11 +131,16 @@ Range span(const void *base, int n_inst, int64_t stride, int64_t elems, size_t e
   return Range{lo, lo + (uintptr_t)(last * (int64_t)esize)};
 }
 
-int check_sizes(int n_inst, int n_head, int n_tok, int n_kv, int hd) {
+// has_mask: the token limit of a masked call (mask rows are staged per token);
+// without a mask (and for the plan helpers) the unmasked limit applies
+int check_sizes(int n_inst, int n_head, int n_tok, int n_kv, int hd, bool has_mask = false) {
   if (n_inst < 1 || n_head < 1 || n_tok < 1 || n_kv < 1 || hd < 1) return FR_ERR_INVALID;
-  if (n_tok > FR_MAX_TOKENS || n_head > FR_MAX_HEADS) return FR_ERR_UNSUPPORTED;
+  if (n_tok > (has_mask ? FR_MAX_TOKENS : FR_MAX_TOKENS_UNMASKED) || n_head > FR_MAX_HEADS)
+    return FR_ERR_UNSUPPORTED;
   if (hd != 64 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
-  if (n_kv > (1 << 26) || (int64_t)n_tok * n_kv > (1 << 30)) return FR_ERR_UNSUPPORTED;
+  if (n_kv > (1 << 26)) return FR_ERR_UNSUPPORTED;
+  // the kernels' 32-bit mask offsets
+  if (has_mask && (int64_t)n_tok * n_kv > (1 << 30)) return FR_ERR_UNSUPPORTED;
   if ((int64_t)n_inst * n_head * n_tok > (1 << 24)) return FR_ERR_UNSUPPORTED;
   return FR_OK;
 }
@@ -155,7 +160,7 @@ int validate(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
              int n_kvh, int64_t kvh_stride, int n_tok, int n_kv, int hd, float scale,
              unsigned flags) {
   if (!q || !k || !v || !out) return FR_ERR_INVALID;
-  int st = check_sizes(n_inst, n_head, n_tok, n_kv, hd);
+  int st = check_sizes(n_inst, n_head, n_tok, n_kv, hd, mask != nullptr);
   if (st != FR_OK) return st;
   // KV heads: a divisor of n_head, each a 16-byte aligned [n_kv][hd] block
   if (n_kvh < 1 || n_head % n_kvh != 0) return FR_ERR_INVALID;
@@ -389,7 +394,7 @@ int fr_qkv_post(const float *qkv, const int32_t *pos, uint16_t *q16, uint16_t *k
                 float q_scale, void *stream) {
   if (!qkv || !pos || !q16 || (!k_cache) != (!v_cache)) return FR_ERR_INVALID;
   if (n_inst < 1 || n_head < 1 || n_kv_head < 1 || n_tok < 1) return FR_ERR_INVALID;
-  if (n_tok > FR_MAX_TOKENS || n_head > FR_MAX_HEADS || n_kv_head > FR_MAX_HEADS)
+  if (n_tok > FR_MAX_TOKENS_UNMASKED || n_head > FR_MAX_HEADS || n_kv_head > FR_MAX_HEADS)
     return FR_ERR_UNSUPPORTED;
   if (hd != 64 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
   if (!std::isfinite(rope_base) || !(rope_base > 0.f) || !std::isfinite(q_scale))

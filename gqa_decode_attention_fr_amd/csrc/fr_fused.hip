@@ -1010,7 +1010,7 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
     case 128: fn = pick_shape<128>(plan.waves, plan.tiles, p.qmode, mm); break;
     case 256: fn = pick_shape<256>(plan.waves, plan.tiles, p.qmode, mm); break;
   }
-  if (!fn || p.n_tok > max_tokens(plan.waves)) return hipErrorInvalidValue;
+  if (!fn || (p.mask && p.n_tok > max_tokens(plan.waves))) return hipErrorInvalidValue;
   if (mm == kMaskReg && p.n_tok > kMaxTok4) return hipErrorInvalidValue;
 
   const int M = p.unit_rows();

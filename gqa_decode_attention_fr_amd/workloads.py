@@ -46,11 +46,12 @@ class Workload:
     q_dtype: str = "f32"  # "f32" or "f16" (pre-rounded handoff)
     sigma_q: float = 1.0
     sigma_kv: float = 1.0
-    mask_kind: str = "zero"   # "zero" | "pad" | "causal_tail"
+    mask_kind: str = "zero"   # "zero" | "pad" | "causal_tail" | "none" (no mask passed)
     k_outlier_frac: float = 0.0
     k_outlier_scale: float = 1.0
     seed: int = 0
     n_kv_head: int = 1   # KV heads; query head h reads KV head h // (n_head // n_kv_head)
+    dynamic_len: bool = False  # valid keys passed as device counts instead of a mask
 
     @property
     def scale(self) -> float:
@@ -65,8 +66,9 @@ class Workload:
         K and V over keys visible to at least one query, Q, the full mask,
         and the fp32 output."""
         qb = 4 if self.q_dtype == "f32" else 2
+        mask_bytes = 0 if self.mask_kind == "none" else self.n_tok * self.n_kv * 2
         per = (2 * self.n_kv_head * self.n_valid * self.hd * 2 + self.M * self.hd * qb
-               + self.n_tok * self.n_kv * 2 + self.M * self.hd * 4)
+               + mask_bytes + self.M * self.hd * 4)
         return per * self.n_inst
 
     def flops(self) -> int:
@@ -100,7 +102,13 @@ GQA_KV8 = Workload("gqa_h32_kv8_hd128_t4_kv4096_x8", n_head=32, n_tok=4, n_kv=40
 SPEC_VERIFY_T64 = Workload("spec_verify_h32_kv8_hd128_t64_kv8192", n_head=32, n_tok=64,
                            n_kv=8192, n_valid=8192, hd=128, n_kv_head=8,
                            mask_kind="causal_tail")
-EXTRA_WORKLOADS = [GQA_KV8, SPEC_VERIFY_T64]
+# The prefix-LM prefill attention of the pages: every one of the 968 prefix
+# tokens attends over the same 968 keys (row-uniform, pad-only mask), so no
+# mask is passed and the padded tail of the 1024-key buffer is excluded by a
+# device-side valid count.
+PREFILL_PI05 = Workload("prefill_pi05_h8_hd256_t968_kv1024", n_head=8, n_tok=968, n_kv=1024,
+                        n_valid=968, hd=256, sigma_kv=0.5, mask_kind="none", dynamic_len=True)
+EXTRA_WORKLOADS = [GQA_KV8, SPEC_VERIFY_T64, PREFILL_PI05]
 
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
@@ -113,7 +121,7 @@ def f16_bits(x: np.ndarray) -> np.ndarray:
 def build_mask(w: Workload) -> np.ndarray:
     """[n_tok, n_kv] f16 bits for the workload's mask kind."""
     m = np.full((w.n_tok, w.n_kv), F16_ZERO, dtype=np.uint16)
-    if w.mask_kind == "zero":
+    if w.mask_kind in ("zero", "none"):   # "none": an all-zero mask that is not passed
         pass
     elif w.mask_kind == "pad":
         m[:, w.n_valid:] = F16_NEG_INF

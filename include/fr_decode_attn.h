@@ -75,8 +75,8 @@ extern "C" {
 typedef enum fr_status {
     FR_OK = 0,
     FR_ERR_INVALID = -1,     /* null/misaligned pointer, bad size, stride or KV-head count, out overlaps an input */
-    FR_ERR_UNSUPPORTED = -2, /* n_tok outside 1..64, hd not 64/128/256, n_head outside 1..1024,
-                                n_kv above 2^26 or n_tok*n_kv above 2^30 */
+    FR_ERR_UNSUPPORTED = -2, /* n_tok above 64 with a mask (16384 without), hd not 64/128/256,
+                                n_head above 1024, n_kv above 2^26 or n_tok*n_kv above 2^30 */
     FR_ERR_CAPTURE = -3,     /* the library workspace would have to grow while the stream is captured */
     FR_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
     FR_ERR_WORKSPACE = -5    /* the caller's workspace is smaller than fr_decode_attn_workspace_size */
@@ -93,7 +93,11 @@ typedef enum fr_status {
 
 /* Limits checked by every entry point. */
 #define FR_MAX_TOKENS 64    /* the pages' window covers q_tokens <= 16; up to 64 (a
-                               speculative-verify window) are taken as well */
+                               speculative-verify window) are taken with a mask */
+#define FR_MAX_TOKENS_UNMASKED 16384 /* without a mask (mask == NULL): every query
+                               row sees the same keys, the prefix-LM prefill of
+                               the pages (its padded tail excluded by n_kv or
+                               by fr_decode_attn_gqa's kv_len) */
 #define FR_MAX_HEADS 1024
 
 /*

@@ -192,6 +192,15 @@ def test_plan_shapes(shape, want):
     assert (p["waves"], p["n_rowblk"], p["n_split"], p["chunk"]) == want
 
 
+def test_unmasked_calls_take_long_query_counts():
+    # a masked call stops at 64 tokens; an unmasked one (prefill) goes on
+    assert call(n_tok=65) == B.FR_ERR_UNSUPPORTED
+    assert call(n_tok=16385, mask=None) == B.FR_ERR_UNSUPPORTED
+    assert call(n_tok=968, mask=None, out=0x900000, flags=0x80) == B.FR_ERR_INVALID  # sizes ok
+    p = B.fr_decode_attn_plan(1, 8, 968, 968, 256, 0)
+    assert p["waves"] == 8 and p["n_rowblk"] * 8 * 16 >= 8 * 968
+
+
 def test_many_tokens_take_eight_waves(monkeypatch):
     monkeypatch.setenv("FR_FORCE_WAVES", "4")
     assert B.fr_decode_attn_plan(1, 8, 16, 1024, 256, 0)["waves"] == 4
@@ -207,7 +216,7 @@ def test_forced_split_count(monkeypatch):
 
 def test_sizes_rejected_by_helpers():
     with pytest.raises(B.FrError) as e:
-        B.fr_decode_attn_workspace_size(1, 8, 65, 64, 256)
+        B.fr_decode_attn_workspace_size(1, 8, 16385, 64, 256)
     assert e.value.status == B.FR_ERR_UNSUPPORTED
     info = (ctypes.c_int * 8)()
     assert B.load().fr_decode_attn_plan(1, 8, 1, 64, 96, 0, info, 8) == B.FR_ERR_UNSUPPORTED
@@ -258,7 +267,7 @@ def qkv_call(**kw):
     (dict(q16=None), B.FR_ERR_INVALID),
     (dict(vc=None), B.FR_ERR_INVALID),                      # K cache without V cache
     (dict(hd=96), B.FR_ERR_UNSUPPORTED),
-    (dict(n_tok=65), B.FR_ERR_UNSUPPORTED),
+    (dict(n_tok=16385), B.FR_ERR_UNSUPPORTED),
     (dict(base=0.0), B.FR_ERR_INVALID),
     (dict(base=float("inf")), B.FR_ERR_INVALID),
     (dict(qscale=float("nan")), B.FR_ERR_INVALID),

@@ -91,3 +91,41 @@ def test_spec_verify_workload_full_size(oracle_mod, variant):
     max_abs, rel = errors(got, want)
     print(f"[parity] {w.name} variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     assert_close(got, want, w.name)
+
+
+def test_prefill_full_size(oracle_mod):
+    """The pages' prefix-LM prefill: 968 query tokens over the same 968 keys of
+    a 1024-row buffer, no mask, the padded tail excluded by a device count
+    (fused) or by n_kv itself (decomposed); every element against the oracle
+    over the valid keys."""
+    import gqa_decode_attention_fr_amd as F
+    w = W.PREFILL_PI05
+    say(f"workload {w.name}")
+    g = W.generate(w)
+    c = dict(g, mask=None)
+    c["k"], c["v"] = g["k"][:, None], g["v"][:, None]
+    got = run_gqa(c, w.n_head, 1, w.n_tok, w.n_kv, w.hd, w.scale, kv_len=[w.n_valid])
+    cv = dict(c, k=np.ascontiguousarray(c["k"][:, :, :w.n_valid]),
+              v=np.ascontiguousarray(c["v"][:, :, :w.n_valid]))
+    want = oracle_gqa(oracle_mod, cv, w.n_head, 1, w.n_tok, w.n_valid, w.hd, w.scale,
+                      oracle_mod.Q_F32)
+    max_abs, rel = errors(got, want)
+    print(f"[parity] {w.name} fused max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got, want, w.name)
+    got_d = run_gqa(cv, w.n_head, 1, w.n_tok, w.n_valid, w.hd, w.scale, flags=DECOMP)
+    max_abs, rel = errors(got_d, want)
+    print(f"[parity] {w.name} decomposed max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got_d, want, w.name + " decomposed")
+
+
+def test_gqa_prefill_f16_query(oracle_mod):
+    say("gqa prefill f16 Q")
+    n_head, n_kvh, n_tok, n_kv, hd, valid = 16, 2, 300, 333, 128, 300
+    c = W.random_case(950, n_head, n_tok, n_kv, hd, q_dtype="f16", mask_kind="none",
+                      n_kv_head=n_kvh)
+    scale = 1.0 / math.sqrt(hd)
+    got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, q_f16=True, kv_len=[valid])
+    cv = dict(c, k=np.ascontiguousarray(c["k"][:, :, :valid]),
+              v=np.ascontiguousarray(c["v"][:, :, :valid]))
+    want = oracle_gqa(oracle_mod, cv, n_head, n_kvh, n_tok, valid, hd, scale, oracle_mod.Q_F16)
+    assert_close(got, want, "gqa prefill")
