@@ -68,6 +68,9 @@ def parse_args(argv=None):
     ap.add_argument("--warm", action="store_true",
                     help="also time the same buffers every call (cache-resident, auxiliary)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-calls", action="store_true",
+                    help="also time a batch as back-to-back single-instance calls (a second "
+                         "grid of the same kernels, so kept out of default runs)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run --steps plain 256 MiB device copies (the reference kernel "
@@ -374,7 +377,7 @@ def run_workload(args, torch, F, W, w):
     }
     ms_graph = graph_region(torch, call, pool.R, args.steps)
     aux["graph_replayed_us_per_call"] = round(ms_graph * 1e3, 3)
-    if w.n_inst > 1:
+    if w.n_inst > 1 and args.single_calls:
         singles = make_single_calls(F, w, pool, flags)
         n_b = max(1, args.steps // 10)
         ms_single, _ = timed_region(torch, F, singles, pool.R, n_b, stream, hook=False)
