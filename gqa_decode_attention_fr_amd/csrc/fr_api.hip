@@ -51,11 +51,14 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
   Plan p;
   const int M = n_head * n_tok;
   p.variant = (flags & FR_VARIANT_DECOMPOSED) ? kDecomposed : kFused;
+  // hd 80 rows (160 bytes) do not fit the fused kernel's power-of-two LDS
+  // staging: the decomposition takes them
+  if (hd == 80) p.variant = kDecomposed;
   const int tiles_total = (int)cdiv(M, 16);
   if (p.variant == kDecomposed) {
     // QK^T and PV kernels: 4 waves, a fixed number of 16-row tiles per wave
     p.waves = 4;
-    p.tiles = hd == 256 ? 1 : (hd == 128 ? 2 : 4);
+    p.tiles = hd == 256 ? 1 : (hd == 128 ? 2 : 4);   // hd 64 and 80: 4
   } else {
     // split kernel: one 16-row tile per wave.  Up to 16 tiles run as row
     // blocks of 4 waves (one per SIMD, 64 rows per workgroup): small row
@@ -137,7 +140,7 @@ int check_sizes(int n_inst, int n_head, int n_tok, int n_kv, int hd, bool has_ma
   if (n_inst < 1 || n_head < 1 || n_tok < 1 || n_kv < 1 || hd < 1) return FR_ERR_INVALID;
   if (n_tok > (has_mask ? FR_MAX_TOKENS : FR_MAX_TOKENS_UNMASKED) || n_head > FR_MAX_HEADS)
     return FR_ERR_UNSUPPORTED;
-  if (hd != 64 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 80 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
   if (n_kv > (1 << 26)) return FR_ERR_UNSUPPORTED;
   // the kernels' 32-bit mask offsets
   if (has_mask && (int64_t)n_tok * n_kv > (1 << 30)) return FR_ERR_UNSUPPORTED;
@@ -259,8 +262,10 @@ int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const
   Plan plan;
   st = fr::make_plan(n_inst * n_kvh, n_head / n_kvh, n_tok, n_kv, hd, flags, &plan);
   if (st != FR_OK) return st;
-  // a device-side key count is honoured by the fused path only
+  // a device-side key count is honoured by the fused path only, and hd 80 by
+  // the decomposed one only
   if (kv_len && plan.variant == fr::kDecomposed) return FR_ERR_UNSUPPORTED;
+  if (hd == 80 && (flags & FR_VARIANT_FUSED)) return FR_ERR_UNSUPPORTED;
   if (caller_ws) {
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
       return FR_ERR_WORKSPACE;
@@ -396,7 +401,7 @@ int fr_qkv_post(const float *qkv, const int32_t *pos, uint16_t *q16, uint16_t *k
   if (n_inst < 1 || n_head < 1 || n_kv_head < 1 || n_tok < 1) return FR_ERR_INVALID;
   if (n_tok > FR_MAX_TOKENS_UNMASKED || n_head > FR_MAX_HEADS || n_kv_head > FR_MAX_HEADS)
     return FR_ERR_UNSUPPORTED;
-  if (hd != 64 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 80 && hd != 128 && hd != 256) return FR_ERR_UNSUPPORTED;
   if (!std::isfinite(rope_base) || !(rope_base > 0.f) || !std::isfinite(q_scale))
     return FR_ERR_INVALID;
   if (!aligned(qkv, 4) || !aligned(pos, 4) || !aligned(q16, 2)) return FR_ERR_INVALID;

@@ -41,11 +41,14 @@ struct QkArgs {
   float scale;
 };
 
+// HD = 80 runs its contraction over 96 dimensions: K's LDS rows and the query
+// fragments are zero past d = 80 (the 16x16x32 MFMA takes 32 at a time).
 template <int HD, int TILES, int QMODE>
 __global__ __launch_bounds__(kThreads) void qk_kernel(QkArgs a) {
-  constexpr int KSTR = HD + 8;
-  constexpr int GPR = HD / 8;
-  constexpr int KS = HD / 32;
+  constexpr int HDP = (HD + 31) / 32 * 32;   // contraction length, padded
+  constexpr int KSTR = HDP + 8;
+  constexpr int GPR = HDP / 8;
+  constexpr int KS = HDP / 32;
   __shared__ __attribute__((aligned(16))) _Float16 sK[KB * KSTR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -62,7 +65,8 @@ __global__ __launch_bounds__(kThreads) void qk_kernel(QkArgs a) {
   for (int u = tid; u < KB * GPR; u += kThreads) {
     const int row = u / GPR, c = u % GPR;
     uint4v val = {0u, 0u, 0u, 0u};
-    if (kb0 + row < a.n_kv) val = *(const uint4v *)(kbase + (int64_t)(kb0 + row) * HD + c * 8);
+    if (kb0 + row < a.n_kv && c * 8 < HD)
+      val = *(const uint4v *)(kbase + (int64_t)(kb0 + row) * HD + c * 8);
     *(uint4v *)(sK + row * KSTR + c * 8) = val;
   }
   __syncthreads();
@@ -79,7 +83,8 @@ __global__ __launch_bounds__(kThreads) void qk_kernel(QkArgs a) {
     const int64_t qrow = r < a.M ? (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      load_q8<QMODE>(qinst, qrow + ks * 32 + g * 8, r < a.M, qh[i][ks], ql[i][ks]);
+      load_q8<QMODE>(qinst, qrow + ks * 32 + g * 8, r < a.M && ks * 32 + g * 8 < HD, qh[i][ks],
+                     ql[i][ks]);
   }
   float4v s[TILES][4];
 #pragma unroll
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(256) void sum_kernel(SumArgs a) {
 
 template <int HD>
 void launch_qk(int qmode, dim3 grid, hipStream_t st, const QkArgs &a) {
-  constexpr int T = (HD == 256) ? 1 : (HD == 128 ? 2 : 4);
+  constexpr int T = (HD == 256) ? 1 : (HD == 128 ? 2 : 4);   // hd 64 and 80: 4
   switch (qmode) {
     case kQHiLo: hipLaunchKernelGGL((qk_kernel<HD, T, kQHiLo>), grid, dim3(kThreads), 0, st, a); break;
     case kQF16: hipLaunchKernelGGL((qk_kernel<HD, T, kQF16>), grid, dim3(kThreads), 0, st, a); break;
@@ -346,6 +351,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   const dim3 qgrid(U * plan.n_rowblk * n_kblk);
   switch (p.hd) {
     case 64: launch_qk<64>(p.qmode, qgrid, stream, qa); break;
+    case 80: launch_qk<80>(p.qmode, qgrid, stream, qa); break;
     case 128: launch_qk<128>(p.qmode, qgrid, stream, qa); break;
     case 256: launch_qk<256>(p.qmode, qgrid, stream, qa); break;
   }
@@ -389,6 +395,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   const dim3 pgrid(U * plan.n_rowblk * plan.n_split);
   switch (p.hd) {
     case 64: launch_pv<64>(pgrid, stream, pa); break;
+    case 80: launch_pv<80>(pgrid, stream, pa); break;
     case 128: launch_pv<128>(pgrid, stream, pa); break;
     case 256: launch_pv<256>(pgrid, stream, pa); break;
   }

@@ -75,7 +75,7 @@ extern "C" {
 typedef enum fr_status {
     FR_OK = 0,
     FR_ERR_INVALID = -1,     /* null/misaligned pointer, bad size, stride or KV-head count, out overlaps an input */
-    FR_ERR_UNSUPPORTED = -2, /* n_tok above 64 with a mask (16384 without), hd not 64/128/256,
+    FR_ERR_UNSUPPORTED = -2, /* n_tok above 64 with a mask (16384 without), hd not 64/80/128/256,
                                 n_head above 1024, n_kv above 2^26 or n_tok*n_kv above 2^30 */
     FR_ERR_CAPTURE = -3,     /* the library workspace would have to grow while the stream is captured */
     FR_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
@@ -99,6 +99,9 @@ typedef enum fr_status {
                                the pages (its padded tail excluded by n_kv or
                                by fr_decode_attn_gqa's kv_len) */
 #define FR_MAX_HEADS 1024
+/* Head sizes: 64, 128 and 256 on every path; 80 (a vision-encoder size) on
+ * the three-launch decomposition only, which the plan then picks (with
+ * FR_VARIANT_FUSED or a kv_len, hd 80 is FR_ERR_UNSUPPORTED). */
 
 /*
  * f32 queries.  q: float32 [n_tok][n_head][hd]; k, v, mask, out as above.
@@ -259,7 +262,7 @@ int fr_decode_attn_profile_events(void *start, void *stop);
  *       positions outside [0, capacity) are not stored.
  * Instance i reads qkv + i*qkv_stride and pos + i*pos_stride (0: shared) and
  * writes q16 + i*q16_stride and the caches + i*cache_stride (ELEMENTS).
- * hd is 64, 128 or 256; 1 <= n_tok <= FR_MAX_TOKENS; rope_base > 0.
+ * hd is 64, 80, 128 or 256; 1 <= n_tok <= FR_MAX_TOKENS_UNMASKED; rope_base > 0.
  * Angles are computed in double precision, the rotations in fp32, each output
  * rounded to f16 nearest-even.  No output may overlap an input or another
  * output.  Returns FR_OK or a negative fr_status.

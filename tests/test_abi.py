@@ -147,6 +147,7 @@ def test_single_entry_points_validate_too():
 SHAPES = [(1, 8, 1, 64, 256), (18, 8, 10, 1024, 256), (1, 16, 16, 4096, 128),
           (1, 8, 16, 2048, 256), (1, 32, 16, 32768, 128), (3, 5, 7, 1000, 64), (1, 1, 1, 1, 64),
           (1, 8, 24, 2000, 256), (2, 4, 64, 4096, 128), (1, 1, 17, 77, 64)]
+SHAPES_80 = [(1, 8, 10, 1000, 80), (2, 16, 256, 256, 80)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -162,7 +163,7 @@ def test_plan_covers_keys_and_rows(shape, flags):
     assert p["grid"] == n_inst * p["n_rowblk"] * p["n_split"]
     tiles_total = -(-M // 16)
     if flags:
-        assert p["waves"] == 4 and p["tiles"] == {256: 1, 128: 2, 64: 4}[hd]
+        assert p["waves"] == 4 and p["tiles"] == {256: 1, 128: 2, 80: 4, 64: 4}[hd]
     else:
         # 8 waves above 16 tiles, and for more tokens than 4 waves stage mask rows for
         assert p["tiles"] == 1 and p["waves"] == (4 if tiles_total <= 16 and n_tok <= 16 else 8)
@@ -190,6 +191,24 @@ def test_plan_covers_keys_and_rows(shape, flags):
 def test_plan_shapes(shape, want):
     p = B.fr_decode_attn_plan(*shape, 0)
     assert (p["waves"], p["n_rowblk"], p["n_split"], p["chunk"]) == want
+
+
+@pytest.mark.parametrize("shape", SHAPES_80)
+def test_plan_covers_keys_and_rows_at_hd80(shape):
+    n_inst, n_head, n_tok, n_kv, hd = shape
+    p = B.fr_decode_attn_plan(*shape, 0)
+    assert p["variant"] == 2 and p["waves"] == 4 and p["tiles"] == 4
+    assert p["n_split"] * p["chunk"] >= n_kv > (p["n_split"] - 1) * p["chunk"]
+    assert p["waves"] * p["tiles"] * 16 * p["n_rowblk"] >= n_head * n_tok
+
+
+def test_head_size_80_takes_the_decomposition():
+    assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, 0)["variant"] == 2
+    assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, B.FR_VARIANT_FUSED)["variant"] == 2
+    assert call(hd=80, flags=B.FR_VARIANT_FUSED) == B.FR_ERR_UNSUPPORTED
+    assert gqa_call(hd=80, kvl=0x600000, kvhs=1024 * 80) == B.FR_ERR_UNSUPPORTED
+    ws = B.fr_decode_attn_workspace_size(1, 8, 10, 1000, 80)
+    assert ws >= 80 * 1024 * 6
 
 
 def test_unmasked_calls_take_long_query_counts():

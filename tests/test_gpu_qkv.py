@@ -74,6 +74,7 @@ CASES = [  # n_inst, n_head, n_kv_head, n_tok, hd, capacity, base, q_scale
     (1, 32, 8, 4, 128, 40000, 500000.0, 1.0),
     (3, 16, 2, 1, 64, 64, 10000.0, 0.125),
     (1, 4, 4, 64, 128, 8192, 1000000.0, 0.088),
+    (2, 8, 2, 5, 80, 512, 10000.0, 0.11),            # head size 80
 ]
 
 
