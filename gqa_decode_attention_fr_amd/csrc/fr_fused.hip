@@ -12,8 +12,10 @@
 // run inside one kernel per key split, so scores and probabilities never
 // leave the chip:
 //
-//   workgroup = 4 or 8 waves = (instance, row block, key split); one 16-row
-//   query tile per wave
+//   workgroup = 4 or 8 waves = (unit, row block, key split); one 16-row query
+//   tile per wave.  A unit is one instance's KV head with its group of query
+//   heads (with one KV head, the instance); keys past an instance's valid
+//   count, when one is given, are neither loaded nor weighed
 //   K, V and mask blocks of 64 keys stream global -> LDS with gfx950's 16-byte
 //   direct-to-LDS loads (no register staging) into a two-stage ring, so block
 //   b+1 is in flight while block b is computed.  Waits are explicit vmcnt
@@ -263,9 +265,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   const int l16 = lane & 15;
   const int g = lane >> 4;
 
-  // Workgroup -> (instance, key split, row block).  Workgroup b runs on XCD
-  // b % 8, and each XCD has its own L2: the row blocks of one (instance,
-  // split) pair read the same K/V chunk, so they take workgroups 8 apart (the
+  // Workgroup -> (unit, key split, row block).  Workgroup b runs on XCD
+  // b % 8, and each XCD has its own L2: the row blocks of one (unit, split)
+  // pair read the same K/V chunk, so they take workgroups 8 apart (the
   // same XCD, dispatched close together).  Pairs x = unit*n_split + split go
   // in groups of 8 (fewer in the last group): group gr holds its pairs' row
   // block 0, then row block 1, ...
