@@ -50,16 +50,26 @@
  * the process; failures come back as an fr_status code.  Argument checks run
  * before any HIP call, so a rejected call launches nothing.
  *
+ * Beyond the pages' window (which fixes one KV head, at most 16 query tokens
+ * and a mask): fr_decode_attn_gqa takes several KV heads and device-side
+ * valid key counts; masked calls take up to 64 query tokens and unmasked ones
+ * (the prefix-LM prefill) up to 16384; head size 80 runs on the three-launch
+ * decomposition.  fr_qkv_post (the query/KV producer ahead of the window) and
+ * fr_f16_copy_batch (the batched f32 -> f16 KV tail copies after it) are the
+ * neighbouring steps of the same pull request.
+ *
  * Workspace.  Shapes that split the key range across workgroups keep partial
- * results in a device workspace.  With workspace == NULL (all entry points but
- * fr_decode_attn_ex) the library uses its own per-device buffer, which only
+ * results in a device workspace.  With workspace == NULL (every entry point
+ * without a workspace argument, and fr_decode_attn_ex / fr_decode_attn_gqa
+ * when they get NULL) the library uses its own per-device buffer, which only
  * grows and is never allocated while `stream` is being captured into a graph
  * (the capture-safety rule of the FlashRT-llama.cpp development guide,
  * section "Caches (all capture-safe)"): a call that would need to grow it
  * during capture returns FR_ERR_CAPTURE; call fr_decode_attn_reserve before
  * capturing.  Calls that share the library workspace must be ordered on one
  * stream (or otherwise serialised); concurrent calls on different streams of
- * one device must each pass their own workspace to fr_decode_attn_ex.
+ * one device must each pass their own workspace to fr_decode_attn_ex (or
+ * fr_decode_attn_gqa).
  */
 #ifndef FR_DECODE_ATTN_H
 #define FR_DECODE_ATTN_H
