@@ -70,7 +70,7 @@ def run_qkv(qkv, pos, n_head, n_kvh, hd, capacity, base, q_scale, cache_fill=CAN
 
 
 CASES = [  # n_inst, n_head, n_kv_head, n_tok, hd, capacity, base, q_scale
-    (2, 8, 1, 10, 256, 1024, 10000.0, 0.0625),      # the pi0.5 suffix shape
+    (18, 8, 1, 10, 256, 1024, 10000.0, 0.0625),     # the pi0.5 step, as benchmarked
     (1, 32, 8, 4, 128, 40000, 500000.0, 1.0),
     (3, 16, 2, 1, 64, 64, 10000.0, 0.125),
     (1, 4, 4, 64, 128, 8192, 1000000.0, 0.088),
