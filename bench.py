@@ -334,7 +334,8 @@ def run_workload(args, torch, F, W, w):
         flags |= F.FR_Q_ROUND_F16
     # several KV heads run as n_inst*n_kv_head units of n_head/n_kv_head heads
     units, grp = w.n_inst * w.n_kv_head, w.n_head // w.n_kv_head
-    plan = F.fr_decode_attn_plan(units, grp, w.n_tok, w.n_kv, w.hd, flags)
+    plan_flags = flags | (F.FR_PLAN_UNMASKED if w.mask_kind == "none" else 0)
+    plan = F.fr_decode_attn_plan(units, grp, w.n_tok, w.n_kv, w.hd, plan_flags)
     g = W.generate(w)
     pool = Pool(torch, w, g, args.pool_gib * (1 << 30))
     F.fr_decode_attn_reserve(units, grp, w.n_tok, w.n_kv, w.hd, flags)

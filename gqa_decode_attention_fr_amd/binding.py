@@ -27,6 +27,7 @@ FR_Q_F16 = 1
 FR_Q_ROUND_F16 = 0x1
 FR_VARIANT_FUSED = 0x2
 FR_VARIANT_DECOMPOSED = 0x4
+FR_PLAN_UNMASKED = 0x8
 
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",

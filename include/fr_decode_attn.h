@@ -100,6 +100,8 @@ typedef enum fr_status {
 #define FR_Q_ROUND_F16 0x1u        /* f32 q: round to f16 once, as the pages' gather does */
 #define FR_VARIANT_FUSED 0x2u      /* force the fused single-pass split-KV variant */
 #define FR_VARIANT_DECOMPOSED 0x4u /* force the three-launch QK^T -> softmax -> PV variant */
+#define FR_PLAN_UNMASKED 0x8u      /* plan/workspace helpers: for calls with mask == NULL
+                                      (calls themselves set or clear it from their mask) */
 
 /* Limits checked by every entry point. */
 #define FR_MAX_TOKENS 64    /* the pages' window covers q_tokens <= 16; up to 64 (a
@@ -212,7 +214,9 @@ int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k,
 /* Device workspace bytes a call with these sizes and flags needs (0 if none),
  * or 0 with *status set when the sizes are rejected (status may be NULL).
  * The size does not depend on the query format, so it also suits
- * fr_decode_attn_q16 and FR_Q_F16 calls. */
+ * fr_decode_attn_q16 and FR_Q_F16 calls.  Without FR_PLAN_UNMASKED it covers
+ * calls with and without a mask (the plan of an unmasked call with many rows
+ * differs); with it, unmasked calls only. */
 size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv,
                                      int hd, unsigned flags, int *status);
 
@@ -224,7 +228,8 @@ int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
 
 /*
  * The launch plan a call with these sizes and flags would use (the same for
- * every query format), for tests and benchmarks.  Fills up to n_info ints of
+ * every query format; pass FR_PLAN_UNMASKED for a call with mask == NULL),
+ * for tests and benchmarks.  Fills up to n_info ints of
  * info[]:
  *   [0] variant (1 fused, 2 decomposed)  [1] key splits per instance
  *   [2] keys per split                   [3] waves per workgroup

@@ -202,6 +202,27 @@ def test_plan_covers_keys_and_rows_at_hd80(shape):
     assert p["waves"] * p["tiles"] * 16 * p["n_rowblk"] >= n_head * n_tok
 
 
+def test_unmasked_prefill_plans_four_wave_row_blocks():
+    """An unmasked call with many rows (the prefill) plans 4-wave row blocks
+    and fewer key splits; masked calls keep their plan; the workspace size
+    without the bit covers both."""
+    shape = (1, 8, 968, 1024, 256)
+    masked = B.fr_decode_attn_plan(*shape, 0)
+    unmasked = B.fr_decode_attn_plan(*shape, B.FR_PLAN_UNMASKED)
+    assert (masked["waves"], masked["n_split"]) == (8, 4)
+    assert (unmasked["waves"], unmasked["n_split"], unmasked["n_rowblk"]) == (4, 2, 121)
+    both = B.fr_decode_attn_workspace_size(*shape, 0)
+    only = B.fr_decode_attn_workspace_size(*shape, B.FR_PLAN_UNMASKED)
+    rows = 8 * 968
+    assert only == -(-(2 * rows * 256 * 4 + 2 * rows * 8) // 256) * 256
+    assert both == -(-(4 * rows * 256 * 4 + 4 * rows * 8) // 256) * 256 >= only
+    # few rows: the bit changes nothing; more than 16 tokens unmasked may stay at 4 waves
+    assert B.fr_decode_attn_plan(18, 8, 10, 1024, 256, B.FR_PLAN_UNMASKED) == \
+        B.fr_decode_attn_plan(18, 8, 10, 1024, 256, 0)
+    assert B.fr_decode_attn_plan(1, 1, 40, 500, 128, B.FR_PLAN_UNMASKED)["waves"] == 4
+    assert B.fr_decode_attn_plan(1, 1, 40, 500, 128, 0)["waves"] == 8
+
+
 def test_head_size_80_takes_the_decomposition():
     assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, 0)["variant"] == 2
     assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, B.FR_VARIANT_FUSED)["variant"] == 2
