@@ -205,3 +205,84 @@ def test_graph_replays_follow_device_key_counts():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {step} with counts {new}"
+
+
+def _gqa_selector_case(n_inst, n_head, n_kvh, n_tok, n_kv, hd, seed):
+    """Per KV head, K_j = 2048 e_j for j < min(hd, n_kv); query row (t, h)
+    is e_{pi}: its logits are 128 at key pi of its own KV head and 0
+    elsewhere, so exp(-128) vanishes in fp32 and out[t][h] must be V[h/G][pi]
+    bit for bit.  V differs between KV heads, so a row that reads another KV
+    head's keys or values fails."""
+    rng = np.random.default_rng(seed)
+    n_dir = min(hd, n_kv)
+    M = n_head * n_tok
+    pi = (np.arange(n_inst * M).reshape(n_inst, n_tok, n_head) * 29 + 5) % n_dir
+    k = np.zeros((n_inst, n_kvh, n_kv, hd), dtype=np.float64)
+    k[:, :, np.arange(n_dir), np.arange(n_dir)] = 2048.0
+    q = np.zeros((n_inst, n_tok, n_head, hd), dtype=np.float32)
+    for i in range(n_inst):
+        for t in range(n_tok):
+            q[i, t, np.arange(n_head), pi[i, t]] = 1.0
+    v = W.f16_bits(rng.standard_normal((n_inst, n_kvh, n_kv, hd)))
+    case = {"q": q, "k": W.f16_bits(k), "v": v,
+            "mask": np.zeros((n_inst, n_tok, n_kv), dtype=np.uint16)}
+    return case, pi
+
+
+SELECT = [  # n_inst, n_head, n_kv_head, n_tok, n_kv, hd
+    (2, 8, 4, 3, 200, 128),
+    (1, 32, 8, 16, 1024, 128),
+    (3, 12, 3, 5, 100, 64),
+    (1, 16, 2, 10, 968, 256),
+    (1, 8, 2, 4, 90, 80),       # head size 80: the decomposition
+]
+
+
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+@pytest.mark.parametrize("shape", SELECT, ids=lambda s: "n{}_h{}_g{}_t{}_kv{}_d{}".format(*s))
+def test_gqa_selector_bit_exact(shape, variant):
+    n_inst, n_head, n_kvh, n_tok, n_kv, hd = shape
+    if hd == 80 and variant == FUSED:
+        pytest.skip("head size 80 runs on the decomposition only")
+    say(f"gqa selector {shape} variant={variant}")
+    c, pi = _gqa_selector_case(n_inst, n_head, n_kvh, n_tok, n_kv, hd, SELECT.index(shape))
+    got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, 1.0 / 16, flags=variant)
+    vf = c["v"].view(np.float16).astype(np.float32)
+    G = n_head // n_kvh
+    want = np.empty_like(got)
+    for i in range(n_inst):
+        for t in range(n_tok):
+            for h in range(n_head):
+                want[i, t, h] = vf[i, h // G, pi[i, t, h]]
+    assert np.array_equal(got, want)
+
+
+def test_gqa_writes_only_its_output_and_repeats_bitwise():
+    """Guard bands before, between and after the instances' outputs stay
+    untouched, and a second call gives the same bits."""
+    import gqa_decode_attention_fr_amd as F
+    n_inst, n_head, n_kvh, n_tok, n_kv, hd = 3, 16, 4, 6, 1500, 128
+    say("gqa guard bands and determinism")
+    c = W.random_case(1201, n_head, n_tok, n_kv, hd, mask_kind="random", n_inst=n_inst,
+                      n_kv_head=n_kvh)
+    M = n_head * n_tok
+    guard = 4096
+    stride = M * hd + guard                   # a guard band between instances too
+    buf = torch.full((guard + n_inst * stride,), 12345.0, dtype=torch.float32, device="cuda")
+    q, k, v, m = (dev(c[x], torch) for x in ("q", "k", "v", "mask"))
+    outs = []
+    for _ in range(2):
+        buf.fill_(12345.0)
+        out = buf[guard:]
+        F.fr_decode_attn_gqa(q, F.FR_Q_F32, k, v, m, out, n_inst, M * hd, n_kvh * n_kv * hd,
+                             n_tok * n_kv, stride, n_head, n_kvh, n_kv * hd, n_tok, n_kv, hd,
+                             1.0 / math.sqrt(hd))
+        torch.cuda.synchronize()
+        host = buf.cpu().numpy()
+        written = np.zeros(host.size, dtype=bool)
+        for i in range(n_inst):
+            written[guard + i * stride:guard + i * stride + M * hd] = True
+        assert (host[~written] == 12345.0).all()
+        assert np.isfinite(host[written]).all() and (host[written] != 12345.0).mean() > 0.99
+        outs.append(host[written].copy())
+    assert np.array_equal(outs[0], outs[1])
