@@ -473,22 +473,31 @@ int fr_f16_copy_batch(const fr_f16_copy *copies, int n_copies, void *stream) {
     return FR_ERR_INVALID;
   std::vector<fr::CopyDesc> run;
   run.reserve(n_copies);
-  std::vector<Range> src_r, dst_r;
+  struct Tagged {
+    Range r;
+    bool dst;
+  };
+  std::vector<Tagged> ranges;
+  ranges.reserve(2 * (size_t)n_copies);
   for (int i = 0; i < n_copies; ++i) {
     const fr_f16_copy &c = copies[i];
     if (c.n < 0) return FR_ERR_INVALID;
     if (c.n == 0) continue;
     if (!c.src || !c.dst || !aligned(c.src, 4) || !aligned(c.dst, 2)) return FR_ERR_INVALID;
-    src_r.push_back(span(c.src, 1, 0, c.n, 4));
-    dst_r.push_back(span(c.dst, 1, 0, c.n, 2));
+    ranges.push_back(Tagged{span(c.src, 1, 0, c.n, 4), false});
+    ranges.push_back(Tagged{span(c.dst, 1, 0, c.n, 2), true});
     run.push_back(fr::CopyDesc{c.src, c.dst, c.n});
   }
-  // no destination may overlap a source or another destination
-  for (size_t i = 0; i < dst_r.size(); ++i) {
-    for (size_t j = 0; j < src_r.size(); ++j)
-      if (overlaps(dst_r[i], src_r[j])) return FR_ERR_INVALID;
-    for (size_t j = i + 1; j < dst_r.size(); ++j)
-      if (overlaps(dst_r[i], dst_r[j])) return FR_ERR_INVALID;
+  // No destination may overlap a source or another destination (sources may
+  // overlap each other).  Sorted by start, a range overlaps an earlier one
+  // exactly when it starts below the largest earlier end.
+  std::sort(ranges.begin(), ranges.end(),
+            [](const Tagged &a, const Tagged &b) { return a.r.lo < b.r.lo; });
+  uintptr_t end_any = 0, end_dst = 0;
+  for (const Tagged &t : ranges) {
+    if (t.r.lo < (t.dst ? end_any : end_dst)) return FR_ERR_INVALID;
+    end_any = std::max(end_any, t.r.hi);
+    if (t.dst) end_dst = std::max(end_dst, t.r.hi);
   }
   if (run.empty()) return FR_OK;
   const hipError_t err = fr::launch_f16_copies(run.data(), (int)run.size(), (hipStream_t)stream);

@@ -319,3 +319,19 @@ def qkv_call(**kw):
 ])
 def test_qkv_post_rejected_before_any_launch(kw, status):
     assert qkv_call(**kw) == status
+
+
+def test_copy_batch_overlap_check_scales():
+    """4096 copies, the only overlap between the first and the last destination
+    (far apart in the list): rejected, and quickly (the check sorts the ranges
+    instead of comparing every pair)."""
+    import time
+    n = 4096
+    entries = [(0x10000000 + i * 0x1000, 0x40000000 + i * 0x1000, 256) for i in range(n)]
+    entries[-1] = (entries[-1][0], entries[0][1] + 64, 256)     # lands inside destination 0
+    t = time.perf_counter()
+    assert copy_call(entries) == B.FR_ERR_INVALID
+    assert time.perf_counter() - t < 0.5
+    # overlapping sources alone are fine to validate (still rejected here by a bad size)
+    entries = [(0x10000000, 0x40000000 + i * 0x1000, 256) for i in range(8)] + [(Q, K, -1)]
+    assert copy_call(entries) == B.FR_ERR_INVALID
