@@ -44,7 +44,7 @@ PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense f16 matrix cores
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["gqa_decode_attention_fr_amd/csrc/fr_fused.hip",
                   "gqa_decode_attention_fr_amd/csrc/fr_device.h",
-                  "gqa_decode_attention_fr_amd/csrc/fr_api.hip"]
+                  "gqa_decode_attention_fr_amd/csrc/fr_plan.hip"]
 
 
 def kernel_hash() -> str:

@@ -143,3 +143,21 @@ def test_graph_replay_equals_eager():
         torch.cuda.synchronize()
         for d, e in zip(dsts, eager):
             assert torch.equal(d.view(torch.int16), e.view(torch.int16)), f"replay {it}"
+
+
+def test_copies_may_share_a_source(oracle_mod):
+    """Sources may overlap (only destinations are checked): three copies of
+    one source, and one of its second half, all equal the oracle's rounding."""
+    import gqa_decode_attention_fr_amd as F
+    say("f16 copy: shared source")
+    rng = np.random.default_rng(13)
+    src = torch.from_numpy(rng.standard_normal(5000).astype(np.float32)).cuda()
+    dsts = [torch.zeros(5000, dtype=torch.float16, device="cuda") for _ in range(3)]
+    half = torch.zeros(2500, dtype=torch.float16, device="cuda")
+    F.fr_f16_copy_batch([(src, d, 5000) for d in dsts] +
+                        [(src.data_ptr() + 4 * 2500, half, 2500)])
+    torch.cuda.synchronize()
+    want = oracle_mod.f16_copy(src.cpu().numpy())
+    for d in dsts:
+        assert np.array_equal(d.cpu().numpy().view(np.uint16), want)
+    assert np.array_equal(half.cpu().numpy().view(np.uint16), want[2500:])
