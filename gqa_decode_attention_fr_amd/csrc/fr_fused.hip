@@ -900,8 +900,8 @@ struct CombineArgs {
   int n_kvh, grp, n_head;
 };
 
-// 256 threads = RW rows x G split groups x (HD/4) columns of 4 consecutive d,
-// with G * RW * HD/4 = 256.  Thread (row, g, c) merges splits g, g+G, g+2G, ...
+// NT threads = RW rows x G split groups x (HD/4) columns of 4 consecutive d,
+// with G * RW * HD/4 = NT (128 or 256).  Thread (row, g, c) merges splits g, g+G, g+2G, ...
 // (R of its loads in flight together); with G > 1 the G group results of a row
 // are then merged in group order through LDS.  Few splits take G = 1 and several
 // rows per workgroup, so every load of a row is in flight at once and no LDS
@@ -910,11 +910,11 @@ struct CombineArgs {
 // A split with no visible key has m_s = -inf and weight 0; a row with no
 // visible key at all is written as zeros.  The merge order is fixed, so the
 // result does not depend on timing.
-template <int HD, int G>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+template <int HD, int G, int NT>
+__global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   constexpr int C = HD / 4;          // float4 columns per row
-  constexpr int RW = 256 / (C * G);  // rows per workgroup
-  static_assert(RW >= 1 && RW * G * C == 256, "thread layout");
+  constexpr int RW = NT / (C * G);   // rows per workgroup
+  static_assert(RW >= 1 && RW * G * C == NT, "thread layout");
   constexpr int R = 8;               // loads in flight per thread per round
   __shared__ float4v s_acc[G > 1 ? RW : 1][G][C];
   __shared__ float s_m[G > 1 ? RW : 1][G][C], s_l[G > 1 ? RW : 1][G][C];
@@ -990,15 +990,29 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 // Split groups of the combine: enough that each thread has at most R = 8 splits
-// to load, and no more (more groups mean fewer rows per workgroup).
+// to load, and no more (more groups mean fewer rows per workgroup).  Where the
+// groups of one row fit in 128 threads and that gives fewer than 1024
+// workgroups, workgroups of 128 threads (twice as many: pi0.5 step -0.22 us
+// per call, f16-Q -0.38); else 256 (larger grids, such as a prefill's, were
+// slower with 128).
 template <int HD>
 hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
   constexpr int C = HD / 4;
   const int rows = c.n_inst * c.M;
   auto go = [&](auto GI) {
-    constexpr int G = decltype(GI)::value < 256 / C ? decltype(GI)::value : 256 / C;
+    constexpr int GN = decltype(GI)::value;   // split groups wanted
+    if constexpr (GN * C <= 128) {
+      constexpr int RW = 128 / (C * GN);
+      const int wgs = (rows + RW - 1) / RW;
+      if (wgs < 1024) {
+        hipLaunchKernelGGL((combine_kernel<HD, GN, 128>), dim3(wgs), dim3(128), 0, stream, c);
+        return hipGetLastError();
+      }
+    }
+    constexpr int G = GN < 256 / C ? GN : 256 / C;
     constexpr int RW = 256 / (C * G);
-    hipLaunchKernelGGL((combine_kernel<HD, G>), dim3((rows + RW - 1) / RW), dim3(256), 0, stream, c);
+    hipLaunchKernelGGL((combine_kernel<HD, G, 256>), dim3((rows + RW - 1) / RW), dim3(256), 0,
+                       stream, c);
     return hipGetLastError();
   };
   const int need = (c.n_split + 7) / 8;   // groups that give each thread <= 8 splits
