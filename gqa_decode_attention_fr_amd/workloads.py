@@ -108,7 +108,11 @@ SPEC_VERIFY_T64 = Workload("spec_verify_h32_kv8_hd128_t64_kv8192", n_head=32, n_
 # device-side valid count.
 PREFILL_PI05 = Workload("prefill_pi05_h8_hd256_t968_kv1024", n_head=8, n_tok=968, n_kv=1024,
                         n_valid=968, hd=256, sigma_kv=0.5, mask_kind="none", dynamic_len=True)
-EXTRA_WORKLOADS = [GQA_KV8, SPEC_VERIFY_T64, PREFILL_PI05]
+# Plain one-token grouped-query decode (32 query heads on 8 KV heads, 8
+# sequences of 4096 keys): each unit has 4 query rows, a quarter of a tile.
+GQA_DECODE_T1 = Workload("gqa_decode_h32_kv8_hd128_t1_kv4096_x8", n_head=32, n_tok=1,
+                         n_kv=4096, n_valid=4096, hd=128, n_inst=8, n_kv_head=8)
+EXTRA_WORKLOADS = [GQA_KV8, GQA_DECODE_T1, SPEC_VERIFY_T64, PREFILL_PI05]
 
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

@@ -100,10 +100,10 @@ def test_gqa_with_one_kv_head_equals_ex():
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("w", [W.GQA_KV8, W.GQA_DECODE_T1], ids=lambda w: w.name)
 @pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
-def test_gqa_workload_full_size(oracle_mod, variant):
-    """The measured several-KV-head workload, every element, both variants."""
-    w = W.GQA_KV8
+def test_gqa_workload_full_size(oracle_mod, variant, w):
+    """The measured several-KV-head workloads, every element, both variants."""
     say(f"workload {w.name} variant={variant}")
     g = W.generate(w)
     got = run_gqa(g, w.n_head, w.n_kv_head, w.n_tok, w.n_kv, w.hd, w.scale, flags=variant)
