@@ -231,8 +231,13 @@ struct Stage {
   uint16_t m[NW * 64 * 8];  // one 16-byte granule per lane: NW*8 token rows of 64 keys
 };
 
-// NW waves per workgroup (4 or 8), TPW 16-row tiles per wave.
-template <int HD, int NW, int TPW, int QMODE, int MASKMODE>
+// NW waves per workgroup (4 or 8), TPW 16-row tiles per wave.  HD is the
+// head size of the LDS layout and the contractions, HDD that of the data in
+// memory: hd 80 runs in the hd-128 layout (HDD = 80 < HD = 128).  The granules
+// of a K/V row past HDD repeat in-row granules: in the scores they meet the
+// query's zero columns (exact zeros), and the output columns past HDD they
+// produce are never stored.
+template <int HD, int NW, int TPW, int QMODE, int MASKMODE, int HDD = HD>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   constexpr int kWaves = NW;
   constexpr int kThreads = NW * 64;
@@ -248,6 +253,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   constexpr int J = 2 * NJ + NJM;             // vector-memory ops per wave per block
   constexpr int KS = HD / 32;
   constexpr int DT = HD / 16;
+  constexpr int GPRD = HDD / 8;               // granules of a row in memory
+  constexpr int DTD = HDD / 16;               // output tiles of 16 columns stored
+  static_assert(HDD <= HD && HDD % 16 == 0 && 2 * GPRD >= GPR, "data row within the layout");
 
   __shared__ __attribute__((aligned(16))) Stage<HD, NW> stg[2];
   Stage<HD, NW> &st0 = stg[0];
@@ -309,11 +317,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       const float4v zero = {0.f, 0.f, 0.f, 0.f};
       if (a.n_split == 1) {
         float *orow = a.out + (int64_t)rinst * a.out_stride +
-                      (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD;
-        for (int dt = 0; dt < DT; ++dt) *(float4v *)(orow + dt * 16 + 4 * g) = zero;
+                      (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HDD;
+        for (int dt = 0; dt < DTD; ++dt) *(float4v *)(orow + dt * 16 + 4 * g) = zero;
       } else {
         const int64_t prow = ((int64_t)inst * a.n_split + split) * a.M + r;
-        for (int dt = 0; dt < DT; ++dt) *(float4v *)(a.part_o + prow * HD + dt * 16 + 4 * g) = zero;
+        for (int dt = 0; dt < DTD; ++dt)
+          *(float4v *)(a.part_o + prow * HDD + dt * 16 + 4 * g) = zero;
         if (g == 0) a.part_ml[prow] = float2v{-INFINITY, 0.f};
       }
     }
@@ -337,8 +346,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     const int r = (wave * NJ + j) * RPI + lane / GPR;
     const int slot = lane % GPR;
     dma_row[j] = r;
-    dma_kofs[j] = 2u * (uint32_t)(r * HD + 8 * (slot ^ swz_k(r, GPR)));
-    dma_vofs[j] = 2u * (uint32_t)(r * HD + 8 * (slot ^ swz_v(r, GPR)));
+    const int ck = slot ^ swz_k(r, GPR), cv = slot ^ swz_v(r, GPR);   // row granules
+    dma_kofs[j] = 2u * (uint32_t)(r * HDD + 8 * (ck < GPRD ? ck : ck - GPRD));
+    dma_vofs[j] = 2u * (uint32_t)(r * HDD + 8 * (cv < GPRD ? cv : cv - GPRD));
   }
   // mask granule of this lane: token t = lin / 8, key group (lin % 8) ^ swz_m(t);
   // byte offset < 2^31 (n_tok * n_kv <= 2^30 is checked by the host)
@@ -355,13 +365,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   // (those keys are dropped by the ragged-block handling of the softmax).
   auto issue = [&](Stage<HD, NW> &s, int kb0, uint32_t (&rmr)[NMR]) __attribute__((always_inline)) {
     const bool full = kb0 + KB <= n_eff;
-    const char *kb = (const char *)(kbase + (int64_t)kb0 * HD);   // uniform
-    const char *vb = (const char *)(vbase + (int64_t)kb0 * HD);
+    const char *kb = (const char *)(kbase + (int64_t)kb0 * HDD);   // uniform
+    const char *vb = (const char *)(vbase + (int64_t)kb0 * HDD);
     const int last = n_eff - 1 - kb0;                               // last valid row
     uint32_t back[NJ];   // bytes from rows past the valid keys back to the last one
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      back[j] = full ? 0u : 2u * (uint32_t)(max(dma_row[j] - last, 0) * HD);
+      back[j] = full ? 0u : 2u * (uint32_t)(max(dma_row[j] - last, 0) * HDD);
       dma16(kb, dma_kofs[j] - back[j], (char *)s.k + (wave * NJ + j) * 1024);
     }
     if (MASKMODE == kMaskDma) {
@@ -417,10 +427,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     const bool in_blk = wave + kWaves * i < a.tpr;   // tile belongs to this row block
     q_on[i] = r < a.M && in_blk;
     // every lane loads (rows out of range read row 0 and are zeroed after the wait)
-    const int64_t rbase = q_on[i] ? (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD : 0;
+    const int64_t rbase = q_on[i] ? (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HDD : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int64_t off = rbase + ks * 32 + g * 8;
+      // columns past HDD read the row's start and are zeroed after the wait
+      const int64_t off = rbase + (ks * 32 + g * 8 < HDD ? ks * 32 + g * 8 : 0);
       if (QMODE == kQF16) {
         qraw[i][ks][0] = gload16((const uint16_t *)qinst + off);
         qraw[i][ks][1] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -453,8 +464,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const float4v zero = {0.f, 0.f, 0.f, 0.f};
-      const float4v x0 = q_on[i] ? qraw[i][ks][0] : zero;
-      const float4v x1 = q_on[i] ? qraw[i][ks][1] : zero;
+      const bool on = q_on[i] && ks * 32 + g * 8 < HDD;
+      const float4v x0 = on ? qraw[i][ks][0] : zero;
+      const float4v x1 = on ? qraw[i][ks][1] : zero;
       if (QMODE == kQF16) {
         qh[i][ks] = __builtin_bit_cast(half8, x0);
         ql[i][ks] = half8{};
@@ -839,14 +851,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       if (a.n_split == 1) {
         const float inv = (l > 0.f) ? 1.f / l : 0.f;   // (a row with no key: 0)
         float *orow = a.out + (int64_t)rinst * a.out_stride +
-                      (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD;
+                      (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HDD;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *(float4v *)(orow + dt * 16 + 4 * g) = o[i][dt] * inv;
+        for (int dt = 0; dt < DTD; ++dt) *(float4v *)(orow + dt * 16 + 4 * g) = o[i][dt] * inv;
       } else {
         const int64_t prow = ((int64_t)inst * a.n_split + split) * a.M + r;
-        float *po = a.part_o + prow * HD;
+        float *po = a.part_o + prow * HDD;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DTD; ++dt)
           __builtin_nontemporal_store(o[i][dt], (float4v *)(po + dt * 16 + 4 * g));
         if (g == 0) a.part_ml[prow] = float2v{m_run[i] * kLog2e, l};
       }
@@ -877,11 +889,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       const int e = k * 64 + lane;
       const int q = e / C4, c = e % C4;
       const int r = tile * 16 + q;
-      if (r >= a.M) continue;
+      if (r >= a.M || 4 * c >= HDD) continue;
       const int64_t prow = ((int64_t)inst * a.n_split + split) * a.M + r;
       // streaming stores: the partials are read once, by the combine kernel
       __builtin_nontemporal_store(*(const float4v *)(t + q * OS + 4 * c),
-                                  (float4v *)(a.part_o + prow * HD + 4 * c));
+                                  (float4v *)(a.part_o + prow * HDD + 4 * c));
     }
     const int r = tile * 16 + l16;
     if (g == 0 && r < a.M) {
@@ -1001,19 +1013,28 @@ hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
   const int rows = c.n_inst * c.M;
   auto go = [&](auto GI) {
     constexpr int GN = decltype(GI)::value;   // split groups wanted
-    if constexpr (GN * C <= 128) {
-      constexpr int RW = 128 / (C * GN);
-      const int wgs = (rows + RW - 1) / RW;
-      if (wgs < 1024) {
-        hipLaunchKernelGGL((combine_kernel<HD, GN, 128>), dim3(wgs), dim3(128), 0, stream, c);
-        return hipGetLastError();
+    if constexpr ((C & (C - 1)) != 0) {
+      // hd 80: 20 columns; workgroups of 160 threads (320 for 16 groups)
+      constexpr int NT = GN * C <= 160 ? 160 : 320;
+      constexpr int RW = NT / (C * GN);
+      hipLaunchKernelGGL((combine_kernel<HD, GN, NT>), dim3((rows + RW - 1) / RW), dim3(NT), 0,
+                         stream, c);
+      return hipGetLastError();
+    } else {
+      if constexpr (GN * C <= 128) {
+        constexpr int RW = 128 / (C * GN);
+        const int wgs = (rows + RW - 1) / RW;
+        if (wgs < 1024) {
+          hipLaunchKernelGGL((combine_kernel<HD, GN, 128>), dim3(wgs), dim3(128), 0, stream, c);
+          return hipGetLastError();
+        }
       }
+      constexpr int G = GN < 256 / C ? GN : 256 / C;
+      constexpr int RW = 256 / (C * G);
+      hipLaunchKernelGGL((combine_kernel<HD, G, 256>), dim3((rows + RW - 1) / RW), dim3(256), 0,
+                         stream, c);
+      return hipGetLastError();
     }
-    constexpr int G = GN < 256 / C ? GN : 256 / C;
-    constexpr int RW = 256 / (C * G);
-    hipLaunchKernelGGL((combine_kernel<HD, G, 256>), dim3((rows + RW - 1) / RW), dim3(256), 0,
-                       stream, c);
-    return hipGetLastError();
   };
   const int need = (c.n_split + 7) / 8;   // groups that give each thread <= 8 splits
   if (need <= 1) return go(std::integral_constant<int, 1>{});
@@ -1025,34 +1046,34 @@ hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
 
 typedef void (*SplitFn)(SplitArgs);
 
-template <int HD, int NW, int TPW, int QMODE>
+template <int HD, int NW, int TPW, int QMODE, int HDD>
 SplitFn pick_mask(int mm) {
   switch (mm) {
-    case kMaskNone: return split_kernel<HD, NW, TPW, QMODE, kMaskNone>;
-    case kMaskDma: return split_kernel<HD, NW, TPW, QMODE, kMaskDma>;
-    case kMaskReg: return split_kernel<HD, NW, TPW, QMODE, kMaskReg>;
+    case kMaskNone: return split_kernel<HD, NW, TPW, QMODE, kMaskNone, HDD>;
+    case kMaskDma: return split_kernel<HD, NW, TPW, QMODE, kMaskDma, HDD>;
+    case kMaskReg: return split_kernel<HD, NW, TPW, QMODE, kMaskReg, HDD>;
     case kMaskReg64:
-      if constexpr (NW == 8) return split_kernel<HD, NW, TPW, QMODE, kMaskReg64>;
+      if constexpr (NW == 8) return split_kernel<HD, NW, TPW, QMODE, kMaskReg64, HDD>;
       return nullptr;
     default: return nullptr;
   }
 }
 
-template <int HD, int NW, int TPW>
+template <int HD, int NW, int TPW, int HDD>
 SplitFn pick_q(int qmode, int mm) {
   switch (qmode) {
-    case kQHiLo: return pick_mask<HD, NW, TPW, kQHiLo>(mm);
-    case kQF16: return pick_mask<HD, NW, TPW, kQF16>(mm);
-    case kQRound: return pick_mask<HD, NW, TPW, kQRound>(mm);
+    case kQHiLo: return pick_mask<HD, NW, TPW, kQHiLo, HDD>(mm);
+    case kQF16: return pick_mask<HD, NW, TPW, kQF16, HDD>(mm);
+    case kQRound: return pick_mask<HD, NW, TPW, kQRound, HDD>(mm);
     default: return nullptr;
   }
 }
 
 // Instantiated shapes: 4 or 8 waves, one 16-row tile per wave.
-template <int HD>
+template <int HD, int HDD = HD>
 SplitFn pick_shape(int nw, int tpw, int qmode, int mm) {
-  if (nw == 4 && tpw == 1) return pick_q<HD, 4, 1>(qmode, mm);
-  if (nw == 8 && tpw == 1) return pick_q<HD, 8, 1>(qmode, mm);
+  if (nw == 4 && tpw == 1) return pick_q<HD, 4, 1, HDD>(qmode, mm);
+  if (nw == 8 && tpw == 1) return pick_q<HD, 8, 1, HDD>(qmode, mm);
   return nullptr;
 }
 
@@ -1068,6 +1089,7 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   SplitFn fn = nullptr;
   switch (p.hd) {
     case 64: fn = pick_shape<64>(plan.waves, plan.tiles, p.qmode, mm); break;
+    case 80: fn = pick_shape<128, 80>(plan.waves, plan.tiles, p.qmode, mm); break;
     case 128: fn = pick_shape<128>(plan.waves, plan.tiles, p.qmode, mm); break;
     case 256: fn = pick_shape<256>(plan.waves, plan.tiles, p.qmode, mm); break;
   }
@@ -1126,6 +1148,7 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   c.n_head = p.n_head;
   switch (p.hd) {
     case 64: return launch_combine<64>(c, stream);
+    case 80: return launch_combine<80>(c, stream);
     case 128: return launch_combine<128>(c, stream);
     case 256: return launch_combine<256>(c, stream);
   }

@@ -25,9 +25,6 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
   const int M = n_head * n_tok;
   const bool unmasked = (flags & FR_PLAN_UNMASKED) != 0;
   p.variant = (flags & FR_VARIANT_DECOMPOSED) ? kDecomposed : kFused;
-  // hd 80 rows (160 bytes) do not fit the fused kernel's power-of-two LDS
-  // staging: the decomposition takes them
-  if (hd == 80) p.variant = kDecomposed;
   const int tiles_total = (int)cdiv(M, 16);
   if (p.variant == kDecomposed) {
     // QK^T and PV kernels: 4 waves, a fixed number of 16-row tiles per wave

@@ -112,7 +112,11 @@ PREFILL_PI05 = Workload("prefill_pi05_h8_hd256_t968_kv1024", n_head=8, n_tok=968
 # sequences of 4096 keys): each unit has 4 query rows, a quarter of a tile.
 GQA_DECODE_T1 = Workload("gqa_decode_h32_kv8_hd128_t1_kv4096_x8", n_head=32, n_tok=1,
                          n_kv=4096, n_valid=4096, hd=128, n_inst=8, n_kv_head=8)
-EXTRA_WORKLOADS = [GQA_KV8, GQA_DECODE_T1, SPEC_VERIFY_T64, PREFILL_PI05]
+# Head size 80: a vision-encoder attention (16 heads, each its own KV head,
+# over 256 patch tokens) for 2 camera views, unmasked.
+VISION_HD80 = Workload("vision_mha_h16_hd80_t256_x2", n_head=16, n_tok=256, n_kv=256,
+                       n_valid=256, hd=80, n_inst=2, n_kv_head=16, mask_kind="none")
+EXTRA_WORKLOADS = [GQA_KV8, GQA_DECODE_T1, SPEC_VERIFY_T64, PREFILL_PI05, VISION_HD80]
 
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

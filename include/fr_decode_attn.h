@@ -53,8 +53,8 @@
  * Beyond the pages' window (which fixes one KV head, at most 16 query tokens
  * and a mask): fr_decode_attn_gqa takes several KV heads and device-side
  * valid key counts; masked calls take up to 64 query tokens and unmasked ones
- * (the prefix-LM prefill) up to 16384; head size 80 runs on the three-launch
- * decomposition.  fr_qkv_post (the query/KV producer ahead of the window) and
+ * (the prefix-LM prefill) up to 16384; head size 80 is taken as well.
+ * fr_qkv_post (the query/KV producer ahead of the window) and
  * fr_f16_copy_batch (the batched f32 -> f16 KV tail copies after it) are the
  * neighbouring steps of the same pull request.
  *
@@ -111,9 +111,8 @@ typedef enum fr_status {
                                the pages (its padded tail excluded by n_kv or
                                by fr_decode_attn_gqa's kv_len) */
 #define FR_MAX_HEADS 1024
-/* Head sizes: 64, 128 and 256 on every path; 80 (a vision-encoder size) on
- * the three-launch decomposition only, which the plan then picks (with
- * FR_VARIANT_FUSED or a kv_len, hd 80 is FR_ERR_UNSUPPORTED). */
+/* Head sizes: 64, 80 (a vision-encoder size), 128 and 256, on both variants;
+ * the fused kernel runs hd 80 in its hd-128 layout. */
 
 /*
  * f32 queries.  q: float32 [n_tok][n_head][hd]; k, v, mask, out as above.

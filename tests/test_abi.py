@@ -194,12 +194,21 @@ def test_plan_shapes(shape, want):
 
 
 @pytest.mark.parametrize("shape", SHAPES_80)
-def test_plan_covers_keys_and_rows_at_hd80(shape):
+@pytest.mark.parametrize("flags", [0, B.FR_VARIANT_DECOMPOSED])
+def test_plan_covers_keys_and_rows_at_hd80(shape, flags):
     n_inst, n_head, n_tok, n_kv, hd = shape
-    p = B.fr_decode_attn_plan(*shape, 0)
-    assert p["variant"] == 2 and p["waves"] == 4 and p["tiles"] == 4
+    p = B.fr_decode_attn_plan(*shape, flags)
+    assert p["variant"] == (2 if flags else 1)
+    assert p["tiles"] == (4 if flags else 1)
     assert p["n_split"] * p["chunk"] >= n_kv > (p["n_split"] - 1) * p["chunk"]
     assert p["waves"] * p["tiles"] * 16 * p["n_rowblk"] >= n_head * n_tok
+    rows = n_inst * p["n_split"] * n_head * n_tok
+    if not flags:   # partials of 80 columns
+        ws = B.fr_decode_attn_workspace_size(*shape, B.FR_PLAN_UNMASKED)
+        plan_u = B.fr_decode_attn_plan(*shape, B.FR_PLAN_UNMASKED)
+        rows_u = n_inst * plan_u["n_split"] * n_head * n_tok
+        assert ws == (0 if plan_u["n_split"] == 1 else -(-(rows_u * 80 * 4 + rows_u * 8) // 256) * 256)
+    assert rows >= 0
 
 
 def test_unmasked_prefill_plans_four_wave_row_blocks():
@@ -223,12 +232,13 @@ def test_unmasked_prefill_plans_four_wave_row_blocks():
     assert B.fr_decode_attn_plan(1, 1, 40, 500, 128, 0)["waves"] == 8
 
 
-def test_head_size_80_takes_the_decomposition():
-    assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, 0)["variant"] == 2
-    assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, B.FR_VARIANT_FUSED)["variant"] == 2
-    assert call(hd=80, flags=B.FR_VARIANT_FUSED) == B.FR_ERR_UNSUPPORTED
-    assert gqa_call(hd=80, kvl=0x600000, kvhs=1024 * 80) == B.FR_ERR_UNSUPPORTED
-    ws = B.fr_decode_attn_workspace_size(1, 8, 10, 1000, 80)
+def test_head_size_80_plans():
+    assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, 0)["variant"] == 1
+    assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, B.FR_VARIANT_DECOMPOSED)["variant"] == 2
+    # the decomposition still declines device key counts
+    assert gqa_call(hd=80, kvl=0x600000, kvhs=1024 * 80, flags=B.FR_VARIANT_DECOMPOSED) == \
+        B.FR_ERR_UNSUPPORTED
+    ws = B.fr_decode_attn_workspace_size(1, 8, 10, 1000, 80, B.FR_VARIANT_DECOMPOSED)
     assert ws >= 80 * 1024 * 6
 
 

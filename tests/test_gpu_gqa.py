@@ -234,7 +234,7 @@ SELECT = [  # n_inst, n_head, n_kv_head, n_tok, n_kv, hd
     (1, 32, 8, 16, 1024, 128),
     (3, 12, 3, 5, 100, 64),
     (1, 16, 2, 10, 968, 256),
-    (1, 8, 2, 4, 90, 80),       # head size 80: the decomposition
+    (1, 8, 2, 4, 90, 80),       # head size 80
 ]
 
 
@@ -242,8 +242,6 @@ SELECT = [  # n_inst, n_head, n_kv_head, n_tok, n_kv, hd
 @pytest.mark.parametrize("shape", SELECT, ids=lambda s: "n{}_h{}_g{}_t{}_kv{}_d{}".format(*s))
 def test_gqa_selector_bit_exact(shape, variant):
     n_inst, n_head, n_kvh, n_tok, n_kv, hd = shape
-    if hd == 80 and variant == FUSED:
-        pytest.skip("head size 80 runs on the decomposition only")
     say(f"gqa selector {shape} variant={variant}")
     c, pi = _gqa_selector_case(n_inst, n_head, n_kvh, n_tok, n_kv, hd, SELECT.index(shape))
     got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, 1.0 / 16, flags=variant)
