@@ -44,7 +44,10 @@ PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense f16 matrix cores
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["gqa_decode_attention_fr_amd/csrc/fr_fused.hip",
                   "gqa_decode_attention_fr_amd/csrc/fr_device.h",
-                  "gqa_decode_attention_fr_amd/csrc/fr_plan.hip"]
+                  "gqa_decode_attention_fr_amd/csrc/fr_plan.hip",
+                  "gqa_decode_attention_fr_amd/csrc/fr_decomposed.hip",
+                  "gqa_decode_attention_fr_amd/csrc/fr_copy.hip",
+                  "gqa_decode_attention_fr_amd/csrc/fr_qkv.hip"]
 
 
 def kernel_hash() -> str:
@@ -261,9 +264,10 @@ def achievable_copy_gbps(torch, reps=20):
     return gbps
 
 
-def traffic_for(w_name: str, variant: int):
+def traffic_for(w_name: str, variant=None):
     """HBM bytes per main-kernel launch from the committed rocprofv3 counter
-    summary, or None if missing or taken on different kernel sources."""
+    summary, or None if missing, taken on different kernel sources or (for
+    attention workloads) with another variant."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -475,7 +479,8 @@ def run_copy_workload(args, torch, F):
         "data": "synthetic (normal f32 rows)",
         "config": {"workload": COPY_WORKLOAD, "copies": n_copy, "rows": rows, "hd": hd},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(COPY_WORKLOAD)},
         "aux": {"bytes_per_call": per, "graph_replayed_us_per_call": round(ms_graph * 1e3, 3),
                 "pool_copies": R,
                 "note": "achieved is per whole call (one launch), launch gap included"},
@@ -530,7 +535,8 @@ def run_qkv_workload(args, torch, F):
         "config": {"workload": QKV_WORKLOAD, "n_inst": n_inst, "n_tok": n_tok,
                    "n_head": n_head, "n_kv_head": n_kvh, "hd": hd},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(QKV_WORKLOAD)},
         "aux": {"bytes_per_call": per, "graph_replayed_us_per_call": round(ms_graph * 1e3, 3),
                 "pool_copies": R,
                 "note": "one launch of 180 workgroups; the call is launch-latency bound"},

@@ -53,3 +53,19 @@ def test_committed_traffic_is_well_formed():
     if t["kernel_hash"] != bench.kernel_hash():
         pytest.skip("counters taken on other kernel sources: bench.py reports traffic null")
     assert bench.traffic_for(W.PI05_ACTION_STEP.name, 1) > W.PI05_ACTION_STEP.algorithmic_bytes()
+
+
+def test_committed_traffic_covers_every_workload():
+    """Each line `bench.py --workload all` prints has counter traffic of its own
+    main kernel, at least its algorithmic bytes less the calibration's slack."""
+    with open(bench.TRAFFIC_FILE) as fh:
+        t = json.load(fh)
+    if t["kernel_hash"] != bench.kernel_hash():
+        pytest.skip("counters taken on other kernel sources: bench.py reports traffic null")
+    for w in W.WORKLOADS + W.EXTRA_WORKLOADS:
+        tr = bench.traffic_for(w.name, 1)
+        assert tr is not None and tr > 0.95 * w.algorithmic_bytes(), w.name
+    for name in (bench.COPY_WORKLOAD, bench.QKV_WORKLOAD):
+        rec = t["workloads"][name]
+        assert bench.traffic_for(name) == rec["hbm_bytes_per_launch"]
+        assert rec["hbm_bytes_per_launch"] > 0.95 * rec["algorithmic_bytes_per_launch"]
