@@ -284,3 +284,51 @@ def test_gqa_writes_only_its_output_and_repeats_bitwise():
         assert np.isfinite(host[written]).all() and (host[written] != 12345.0).mean() > 0.99
         outs.append(host[written].copy())
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+def test_kv_blocks_beyond_4_gib(oracle_mod, variant):
+    """KV heads and instances placed 4 to 12 GiB into K and V (64-bit base
+    offsets from kv_stride and kv_head_stride), against the oracle.  The row
+    just before and just after every block holds NaN: a kernel that read it
+    would turn its output rows into NaN."""
+    import gqa_decode_attention_fr_amd as F
+    n_inst, n_head, n_kvh, n_tok, n_kv, hd = 2, 4, 2, 3, 300, 128
+    kvh_stride = (1 << 31) + 37 * hd                # elements: 4 GiB + 37 rows
+    kv_stride = n_kvh * kvh_stride + 11 * hd
+    total = (n_inst - 1) * kv_stride + (n_kvh - 1) * kvh_stride + (n_kv + 1) * hd
+    free, _ = torch.cuda.mem_get_info()
+    if free < 2 * 2 * total + (4 << 30):
+        pytest.skip("needs about 26 GB of free device memory")
+    say(f"kv blocks beyond 4 GiB variant={variant}")
+    c = W.random_case(900, n_head, n_tok, n_kv, hd, q_dtype="f32", mask_kind="random",
+                      n_inst=n_inst, n_kv_head=n_kvh)
+    nan_row = torch.full((hd,), float("nan"), dtype=torch.float16, device="cuda")
+    bufs = []
+    for name in ("k", "v"):
+        t = torch.empty(total, dtype=torch.float16, device="cuda")
+        for i in range(n_inst):
+            for h in range(n_kvh):
+                off = i * kv_stride + h * kvh_stride
+                t[off:off + n_kv * hd] = dev(c[name][i, h].reshape(-1), torch)
+                t[off + n_kv * hd:off + (n_kv + 1) * hd] = nan_row
+                if off >= hd:
+                    t[off - hd:off] = nan_row
+        bufs.append(t)
+    k, v = bufs
+    q, mask = dev(c["q"], torch), dev(c["mask"], torch)
+    M = n_head * n_tok
+    out = torch.full((n_inst, n_tok, n_head, hd), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    scale = 1.0 / math.sqrt(hd)
+    F.fr_decode_attn_gqa(q, F.FR_Q_F32, k, v, mask, out, n_inst, M * hd, kv_stride,
+                         n_tok * n_kv, M * hd, n_head, n_kvh, kvh_stride, n_tok, n_kv, hd,
+                         scale, variant)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del k, v, bufs
+    torch.cuda.empty_cache()
+    want = oracle_gqa(oracle_mod, c, n_head, n_kvh, n_tok, n_kv, hd, scale, oracle_mod.Q_F32)
+    max_abs, rel = errors(got, want)
+    print(f"[parity] kv beyond 4 GiB variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got, want, "kv blocks beyond 4 GiB")
