@@ -449,7 +449,9 @@ def run_copy_workload(args, torch, F):
     n = rows * hd
     per = n_copy * n * 6
     R = max(2, int(math.ceil(args.pool_gib * (1 << 30) / per)))
-    src = torch.randn((R, n_copy, n), dtype=torch.float32, device="cuda") * 0.5
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    src = torch.randn((R, n_copy, n), dtype=torch.float32, device="cuda", generator=gen) * 0.5
     dst = torch.empty((R, n_copy, n), dtype=torch.float16, device="cuda")
     lib = F.binding.load()
     arrs = []
@@ -504,7 +506,10 @@ def run_qkv_workload(args, torch, F):
     per_out = n_inst * n_tok * (n_head + 2 * n_kvh) * hd * 2
     per = per_in + per_out
     R = max(2, int(math.ceil(args.pool_gib * (1 << 30) / (per_in + n_inst * 2 * cap * hd * 2))))
-    qkv = torch.randn((R, n_inst, n_tok, width), dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    qkv = torch.randn((R, n_inst, n_tok, width), dtype=torch.float32, device="cuda",
+                      generator=gen)
     pos = (torch.arange(n_tok, dtype=torch.int32, device="cuda") + 958).repeat(R, n_inst, 1)
     q16 = torch.empty((R, n_inst, n_tok, n_head, hd), dtype=torch.float16, device="cuda")
     kc = torch.zeros((R, n_inst, n_kvh, cap, hd), dtype=torch.float16, device="cuda")
