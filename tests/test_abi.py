@@ -342,3 +342,13 @@ def test_copy_batch_overlap_check_scales():
     t = time.perf_counter()
     assert copy_call(entries) == B.FR_ERR_INVALID
     assert time.perf_counter() - t < 0.5
+
+
+def test_plain_c_consumer_compiles_and_links(tmp_path):
+    """tests/c_consumer.c (run on the GPU by test_gpu_c_consumer.py) builds
+    against the header and the library with gcc alone."""
+    from c_consumer_build import build_consumer
+    if not os.path.exists(os.path.join("/opt/rocm", "lib", "libamdhip64.so")):
+        pytest.skip("HIP runtime not installed")
+    exe = build_consumer(tmp_path / "c_consumer")
+    assert os.path.getsize(exe) > 0
