@@ -209,9 +209,12 @@ def test_hi_lo_query_is_more_accurate_than_rounded(oracle_mod):
     assert errors(hilo, want)[0] < errors(rounded, want)[0]
 
 
-def test_no_writes_outside_out():
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+def test_no_writes_outside_out(variant):
+    """The call writes its output rows and nothing else: guard bands around
+    out keep their canary, and q, k, v and the mask are bitwise unchanged."""
     import gqa_decode_attention_fr_amd as F
-    say("canary guard bands")
+    say(f"canary guard bands and untouched inputs, variant={variant}")
     w = W.PI05_ACTION_STEP
     g = W.generate(w)
     M = w.M
@@ -219,13 +222,17 @@ def test_no_writes_outside_out():
     guard = 4096
     buf = torch.full((n + 2 * guard,), 12345.0, dtype=torch.float32, device="cuda")
     out = buf[guard:guard + n]
-    F.fr_decode_attn_ex(dev(g["q"], torch), F.FR_Q_F32, dev(g["k"], torch), dev(g["v"], torch),
-                        dev(g["mask"], torch), out, w.n_inst, M * w.hd, w.n_kv * w.hd,
-                        w.n_tok * w.n_kv, M * w.hd, w.n_head, w.n_tok, w.n_kv, w.hd, w.scale, 0)
+    ins = {x: dev(g[x], torch) for x in ("q", "k", "v", "mask")}
+    F.fr_decode_attn_ex(ins["q"], F.FR_Q_F32, ins["k"], ins["v"], ins["mask"], out, w.n_inst,
+                        M * w.hd, w.n_kv * w.hd, w.n_tok * w.n_kv, M * w.hd, w.n_head, w.n_tok,
+                        w.n_kv, w.hd, w.scale, variant)
     torch.cuda.synchronize()
     b = buf.cpu().numpy()
     assert np.all(b[:guard] == 12345.0) and np.all(b[-guard:] == 12345.0)
     assert np.all(np.isfinite(b[guard:guard + n]))
+    for x, t in ins.items():
+        after = t.cpu().numpy()
+        assert np.array_equal(after.view(np.uint8), np.ascontiguousarray(g[x]).view(np.uint8)), x
 
 
 def test_masked_keys_do_not_matter():
