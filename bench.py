@@ -264,6 +264,26 @@ def achievable_copy_gbps(torch, reps=20):
     return gbps
 
 
+def achievable_read_gbps(torch, reps=20):
+    """Bytes per second of a plain streaming read: torch's row sums of 1 GiB of
+    float32 (four times the MALL) as 8192 rows, which read every byte once and
+    write 8192 floats.  (A sum to one scalar reaches only about two thirds of
+    this rate; the row form is the fastest simple read torch offers here.)"""
+    n = 256 << 20
+    x = torch.ones(n, dtype=torch.float32, device="cuda").view(8192, -1)
+    s = x.sum(1)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        s = x.sum(1)
+    t1.record()
+    torch.cuda.synchronize()
+    gbps = n * 4 * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del x, s
+    return gbps
+
+
 def traffic_for(w_name: str, variant=None):
     """HBM bytes per main-kernel launch from the committed rocprofv3 counter
     summary, or None if missing, taken on different kernel sources or (for
@@ -390,6 +410,9 @@ def run_workload(args, torch, F, W, w):
     copy_gbps = achievable_copy_gbps(torch)
     aux["achievable_copy_GBps"] = round(copy_gbps, 1)
     aux["kernel_frac_of_achievable_copy"] = round(achieved / copy_gbps, 4)
+    read_gbps = achievable_read_gbps(torch)
+    aux["achievable_read_GBps"] = round(read_gbps, 1)
+    aux["kernel_frac_of_achievable_read"] = round(achieved / read_gbps, 4)
     if args.warm:
         ms_warm, kern_warm = timed_region(torch, F, call, pool.R, args.steps, stream,
                                           same_slot=True)
