@@ -29,6 +29,12 @@ FR_VARIANT_FUSED = 0x2
 FR_VARIANT_DECOMPOSED = 0x4
 FR_PLAN_UNMASKED = 0x8
 
+# shape limits (fr_decode_attn.h)
+FR_MAX_TOKENS = 64
+FR_MAX_TOKENS_UNMASKED = 16384
+FR_MAX_HEADS = 1024
+FR_MAX_COPIES = 4096
+
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
             "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_workspace_size",

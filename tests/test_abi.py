@@ -352,3 +352,18 @@ def test_plain_c_consumer_compiles_and_links(tmp_path):
         pytest.skip("HIP runtime not installed")
     exe = build_consumer(tmp_path / "c_consumer")
     assert os.path.getsize(exe) > 0
+
+
+def test_binding_constants_match_the_header():
+    """Every FR_ constant the binding mirrors has the header's value."""
+    text = open(HEADER).read()
+    defs = {m.group(1): int(m.group(2), 0)
+            for m in re.finditer(r"#define\s+(FR_\w+)\s+(0x[0-9a-fA-F]+|\d+)u?\b", text)}
+    enums = {m.group(1): int(m.group(2))
+             for m in re.finditer(r"\b(FR_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", text)}
+    both = {**defs, **enums}
+    mirrored = [n for n in dir(B) if n.startswith("FR_") and isinstance(getattr(B, n), int)]
+    assert {"FR_MAX_TOKENS", "FR_MAX_TOKENS_UNMASKED", "FR_MAX_HEADS", "FR_PLAN_UNMASKED"} <= set(mirrored)
+    for n in mirrored:
+        assert n in both, n
+        assert getattr(B, n) == both[n], n

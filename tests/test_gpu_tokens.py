@@ -129,3 +129,35 @@ def test_gqa_prefill_f16_query(oracle_mod):
               v=np.ascontiguousarray(c["v"][:, :, :valid]))
     want = oracle_gqa(oracle_mod, cv, n_head, n_kvh, n_tok, valid, hd, scale, oracle_mod.Q_F16)
     assert_close(got, want, "gqa prefill")
+
+
+LARGEST = [  # n_inst, n_head, n_kv_head, n_tok, n_kv, hd, q dtype, mask kind
+    (1, 1, 1, 16384, 200, 64, "f32", "none"),      # the unmasked token limit
+    (1, 2, 2, 16384, 77, 128, "f16", "none"),      # ... with two KV heads, one query head each
+    (1, 1024, 1, 2, 300, 128, "f32", "random"),    # the head limit, masked
+    (1, 1024, 8, 16, 130, 64, "f32", "random"),    # the head limit, 128 query heads per KV head
+]
+
+
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+@pytest.mark.parametrize("shape", LARGEST, ids=lambda s: "n{}_h{}_g{}_t{}_kv{}_d{}_{}_{}".format(*s))
+def test_largest_accepted_row_counts(oracle_mod, shape, variant):
+    """The largest query-token count (no mask) and head count the library
+    accepts, element by element against the oracle."""
+    import gqa_decode_attention_fr_amd as F
+    n_inst, n_head, n_kvh, n_tok, n_kv, hd, qd, mk = shape
+    assert n_tok <= (F.FR_MAX_TOKENS_UNMASKED if mk == "none" else F.FR_MAX_TOKENS)
+    assert n_head <= F.FR_MAX_HEADS
+    say(f"largest {shape} variant={variant}")
+    c = W.random_case(LARGEST.index(shape) + 950, n_head, n_tok, n_kv, hd, q_dtype=qd,
+                      mask_kind=mk, n_inst=n_inst, n_kv_head=n_kvh)
+    if n_kvh == 1:
+        c["k"], c["v"] = c["k"][:, None], c["v"][:, None]
+    scale = 1.0 / math.sqrt(hd)
+    got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=variant,
+                  q_f16=(qd == "f16"))
+    want = oracle_gqa(oracle_mod, c, n_head, n_kvh, n_tok, n_kv, hd, scale,
+                      oracle_mod.Q_F16 if qd == "f16" else oracle_mod.Q_F32)
+    max_abs, rel = errors(got, want)
+    print(f"[parity] largest {shape} variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert_close(got, want, str(shape))
