@@ -78,11 +78,30 @@ CASES = [  # n_inst, n_head, n_kv_head, n_tok, hd, capacity, base, q_scale
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "n{}_h{}_g{}_t{}_d{}".format(*c[:5]))
+def _random_cases(n):
+    """Seeded random shapes: head sizes 64 to 256, 1 to 32 query and 1 to 8 KV
+    heads, 1 to 64 tokens, caches up to 40 000 rows, three RoPE bases."""
+    rng = np.random.default_rng(424242)
+    out = []
+    for _ in range(n):
+        hd = int(rng.choice([64, 80, 128, 256]))
+        n_tok = int(rng.integers(1, 65))
+        cap = int(rng.choice([n_tok + 1 + int(rng.integers(0, 64)), 1024, 8192, 40000]))
+        n_kvh = int(rng.integers(1, 9)) if cap <= 8192 else 1
+        out.append((int(rng.integers(1, 5)), int(rng.integers(1, 33)), n_kvh, n_tok, hd, cap,
+                    float(rng.choice([10000.0, 500000.0, 1000000.0])),
+                    float(rng.uniform(0.05, 1.0))))
+    return out
+
+
+ALL_CASES = CASES + _random_cases(40)
+
+
+@pytest.mark.parametrize("case", ALL_CASES, ids=lambda c: "n{}_h{}_g{}_t{}_d{}_c{}".format(*c[:6]))
 def test_qkv_post_rounding_and_rows(oracle_mod, case):
     n_inst, n_head, n_kvh, n_tok, hd, cap, base, qs = case
     say(f"qkv_post {case}")
-    rng = np.random.default_rng(CASES.index(case) + 40)
+    rng = np.random.default_rng(ALL_CASES.index(case) + 40)
     qkv = rng.standard_normal((n_inst, n_tok, (n_head + 2 * n_kvh) * hd)).astype(np.float32)
     # distinct positions per instance; instance 0 also takes the largest angle
     pos = np.stack([rng.choice(cap - 1, n_tok, replace=False) for _ in range(n_inst)])
