@@ -116,11 +116,7 @@ def make_call(F, w, pool, flags):
 
     kv_len = None
     n_kv = w.n_kv
-    if w.dynamic_len and flags & F.FR_VARIANT_DECOMPOSED:
-        # the decomposed variant takes no device counts: it is given the valid
-        # keys as n_kv (the K/V row stride stays the padded capacity)
-        n_kv = w.n_valid
-    elif w.dynamic_len:   # valid keys as device counts, one per instance
+    if w.dynamic_len:   # valid keys as device counts, one per instance
         import torch
         kv_len = torch.full((w.n_inst,), w.n_valid, dtype=torch.int32, device="cuda")
     kv_len_ptr = None if kv_len is None else kv_len.data_ptr()
@@ -364,8 +360,7 @@ def run_workload(args, torch, F, W, w):
     # several KV heads run as n_inst*n_kv_head units of n_head/n_kv_head heads
     units, grp = w.n_inst * w.n_kv_head, w.n_head // w.n_kv_head
     plan_flags = flags | (F.FR_PLAN_UNMASKED if w.mask_kind == "none" else 0)
-    keys = w.n_valid if (w.dynamic_len and flags & F.FR_VARIANT_DECOMPOSED) else w.n_kv
-    plan = F.fr_decode_attn_plan(units, grp, w.n_tok, keys, w.hd, plan_flags)
+    plan = F.fr_decode_attn_plan(units, grp, w.n_tok, w.n_kv, w.hd, plan_flags)
     g = W.generate(w)
     pool = Pool(torch, w, g, args.pool_gib * (1 << 30))
     F.fr_decode_attn_reserve(units, grp, w.n_tok, w.n_kv, w.hd, flags)

@@ -192,8 +192,6 @@ int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const
   Plan plan;
   st = fr::make_plan(n_inst * n_kvh, n_head / n_kvh, n_tok, n_kv, hd, flags, &plan);
   if (st != FR_OK) return st;
-  // a device-side key count is honoured by the fused path only
-  if (kv_len && plan.variant == fr::kDecomposed) return FR_ERR_UNSUPPORTED;
   if (caller_ws) {
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
       return FR_ERR_WORKSPACE;

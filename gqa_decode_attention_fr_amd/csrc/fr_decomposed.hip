@@ -31,11 +31,18 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
+// Keys of instance i that count: the device count clamped to [0, n_kv], or all
+// n_kv without counts.  Keys past it are hidden from every token and never read.
+__device__ inline int valid_keys(const int32_t *kv_len, int rinst, int n_kv) {
+  return kv_len ? min(max(kv_len[rinst], 0), n_kv) : n_kv;
+}
+
 struct QkArgs {
   const void *q;
   const uint16_t *k;
   float *s;
   int64_t q_stride, kv_stride, kvh_stride;
+  const int32_t *kv_len;   // per-instance valid key counts, or null
   int M, n_kv, kv_pad, n_rowblk, n_kblk;
   int n_kvh, grp, n_head;
   float scale;
@@ -61,11 +68,12 @@ __global__ __launch_bounds__(kThreads) void qk_kernel(QkArgs a) {
   const int kvh = inst % a.n_kvh, rinst = inst / a.n_kvh;
   const int kb0 = kblk * KB;
   const uint16_t *kbase = a.k + (int64_t)rinst * a.kv_stride + (int64_t)kvh * a.kvh_stride;
+  const int n_eff = valid_keys(a.kv_len, rinst, a.n_kv);
 
   for (int u = tid; u < KB * GPR; u += kThreads) {
     const int row = u / GPR, c = u % GPR;
     uint4v val = {0u, 0u, 0u, 0u};
-    if (kb0 + row < a.n_kv && c * 8 < HD)
+    if (kb0 + row < n_eff && c * 8 < HD)
       val = *(const uint4v *)(kbase + (int64_t)(kb0 + row) * HD + c * 8);
     *(uint4v *)(sK + row * KSTR + c * 8) = val;
   }
@@ -123,6 +131,7 @@ struct SoftmaxArgs {
   const uint16_t *mask;
   uint16_t *p;
   int64_t mask_stride;
+  const int32_t *kv_len;   // per-instance valid key counts, or null
   int M, grp, n_kvh, n_tok, n_kv, kv_pad, rows;   // rows = units * M
 };
 
@@ -134,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(SoftmaxArgs a) {
   if (row >= a.rows) return;
   // unit row r of unit u = row / M is token r / grp of instance u / n_kvh
   const int inst = row / a.M / a.n_kvh, r = row % a.M, t = r / a.grp;
+  const int n_eff = valid_keys(a.kv_len, inst, a.n_kv);
   const float *srow = a.s + (int64_t)row * a.kv_pad;
   const uint16_t *mrow =
       a.mask ? a.mask + (int64_t)inst * a.mask_stride + (int64_t)t * a.n_kv : nullptr;
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(SoftmaxArgs a) {
     return (srow[j] + mk) * kLog2e;
   };
   float m = -INFINITY, l = 0.f;
-  for (int j = lane; j < a.n_kv; j += 64) {
+  for (int j = lane; j < n_eff; j += 64) {
     const float x = logit2(j);
     if (x == -INFINITY) continue;
     if (x > m) {
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(SoftmaxArgs a) {
   uint16_t *prow = a.p + (int64_t)row * a.kv_pad;
   for (int j = lane; j < a.kv_pad; j += 64) {
     float pj = 0.f;
-    if (j < a.n_kv && m != -INFINITY) pj = fast_exp2(logit2(j) - m) * inv;
+    if (j < n_eff && m != -INFINITY) pj = fast_exp2(logit2(j) - m) * inv;
     prow[j] = __builtin_bit_cast(uint16_t, (_Float16)pj);
   }
 }
@@ -177,6 +187,7 @@ struct PvArgs {
   float *out;
   float *part;
   int64_t kv_stride, kvh_stride, out_stride;
+  const int32_t *kv_len;   // per-instance valid key counts, or null
   int M, n_kv, kv_pad, n_rowblk, n_split, chunk;
   int n_kvh, grp, n_head;
 };
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(PvArgs a) {
   const int kvh = inst % a.n_kvh, rinst = inst / a.n_kvh;
   const uint16_t *vbase = a.v + (int64_t)rinst * a.kv_stride + (int64_t)kvh * a.kvh_stride;
   const int key_begin = split * a.chunk;
-  const int key_end = min(key_begin + a.chunk, a.n_kv);
+  const int key_end = min(key_begin + a.chunk, valid_keys(a.kv_len, rinst, a.n_kv));
   const int tile0 = rowblk * (kWaves * TILES) + wave * TILES;
   const bool active = tile0 * 16 < a.M;
 
@@ -341,6 +352,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   qa.n_head = p.n_head;
   qa.M = M;
   qa.n_kv = p.n_kv;
+  qa.kv_len = p.kv_len;
   qa.kv_pad = kv_pad;
   qa.n_rowblk = plan.n_rowblk;
   qa.n_kblk = n_kblk;
@@ -368,6 +380,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   sa.n_kvh = p.n_kvh;
   sa.n_tok = p.n_tok;
   sa.n_kv = p.n_kv;
+  sa.kv_len = p.kv_len;
   sa.kv_pad = kv_pad;
   sa.rows = U * M;
   hipLaunchKernelGGL(softmax_kernel, dim3((sa.rows + kWaves - 1) / kWaves), dim3(kThreads), 0,
@@ -388,6 +401,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   pa.n_head = p.n_head;
   pa.M = M;
   pa.n_kv = p.n_kv;
+  pa.kv_len = p.kv_len;
   pa.kv_pad = kv_pad;
   pa.n_rowblk = plan.n_rowblk;
   pa.n_split = plan.n_split;

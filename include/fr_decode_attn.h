@@ -197,9 +197,8 @@ int fr_decode_attn_ex(const void *q, int q_format, const uint16_t *k,
  * they run, so a graph captured once replays with the counts the array holds
  * at replay time, while n_kv (the padded capacity, the mask's row stride)
  * stays fixed.  The key splits are planned for n_kv; splits past the valid
- * count finish at once.  A row whose keys are all hidden is zero.  The
- * decomposed variant does not take kv_len (FR_ERR_UNSUPPORTED with
- * FR_VARIANT_DECOMPOSED).
+ * count finish at once.  A row whose keys are all hidden is zero.  Both
+ * variants take it.
  */
 int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k,
                        const uint16_t *v, const uint16_t *mask,

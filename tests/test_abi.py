@@ -122,7 +122,6 @@ def gqa_call(**kw):
     (dict(n_tok=65), B.FR_ERR_UNSUPPORTED),
     (dict(q=None), B.FR_ERR_INVALID),
     (dict(kvl=0x600002), B.FR_ERR_INVALID),                  # misaligned key counts
-    (dict(kvl=0x600000, flags=B.FR_VARIANT_DECOMPOSED), B.FR_ERR_UNSUPPORTED),
 ])
 def test_gqa_rejected_before_any_launch(kw, status):
     assert gqa_call(**kw) == status
@@ -235,9 +234,6 @@ def test_unmasked_prefill_plans_four_wave_row_blocks():
 def test_head_size_80_plans():
     assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, 0)["variant"] == 1
     assert B.fr_decode_attn_plan(1, 8, 10, 1000, 80, B.FR_VARIANT_DECOMPOSED)["variant"] == 2
-    # the decomposition still declines device key counts
-    assert gqa_call(hd=80, kvl=0x600000, kvhs=1024 * 80, flags=B.FR_VARIANT_DECOMPOSED) == \
-        B.FR_ERR_UNSUPPORTED
     ws = B.fr_decode_attn_workspace_size(1, 8, 10, 1000, 80, B.FR_VARIANT_DECOMPOSED)
     assert ws >= 80 * 1024 * 6
 

@@ -143,10 +143,11 @@ KV_LEN = [  # n_head, n_kv_head, n_tok, n_kv, hd, mask kind, valid counts per in
 ]
 
 
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
 @pytest.mark.parametrize("shape", KV_LEN, ids=lambda s: "h{}_g{}_t{}_kv{}_d{}_{}".format(*s[:6]))
-def test_device_valid_key_counts(oracle_mod, shape):
+def test_device_valid_key_counts(oracle_mod, shape, variant):
     n_head, n_kvh, n_tok, n_kv, hd, mk, lens = shape
-    say(f"kv_len {shape}")
+    say(f"kv_len {shape} variant={variant}")
     c = W.random_case(KV_LEN.index(shape) + 700, n_head, n_tok, n_kv, hd, mask_kind=mk,
                       n_inst=len(lens), n_kv_head=n_kvh)
     if n_kvh == 1:
@@ -154,10 +155,11 @@ def test_device_valid_key_counts(oracle_mod, shape):
     scale = 1.0 / math.sqrt(hd)
     c_or, kv_nan = _hide_past(c, lens, n_kv)
     gpu_in = dict(c)
-    got = run_gqa(gpu_in, n_head, n_kvh, n_tok, n_kv, hd, scale, kv_len=lens, kv_override=kv_nan)
+    got = run_gqa(gpu_in, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=variant, kv_len=lens,
+                  kv_override=kv_nan)
     want = oracle_gqa(oracle_mod, c_or, n_head, n_kvh, n_tok, n_kv, hd, scale, oracle_mod.Q_F32)
     max_abs, rel = errors(got, want)
-    print(f"[parity] kv_len {shape} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    print(f"[parity] kv_len {shape} variant={variant} max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     assert_close(got, want, str(shape))
     for i, L in enumerate(lens):
         if L <= 0:

@@ -59,9 +59,10 @@ def test_hd80_parity(oracle_mod, shape, variant):
         assert np.array_equal(got[:, 0], np.zeros_like(got[:, 0]))
 
 
-def test_hd80_device_key_counts(oracle_mod):
-    """The fused hd-80 kernel with device key counts (the padded tail of K/V
-    set to NaN on the GPU side: a load of it would poison the output)."""
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+def test_hd80_device_key_counts(oracle_mod, variant):
+    """Head size 80 with device key counts, both variants (the padded tail of
+    K/V set to NaN on the GPU side: a load of it would poison the output)."""
     n_inst, n_head, n_kvh, n_tok, n_kv, hd = 3, 16, 2, 5, 700, 80
     lens = [700, 333, 0]
     say("hd80 kv_len")
@@ -74,7 +75,8 @@ def test_hd80_device_key_counts(oracle_mod):
         kg[i, :, L:] = 0x7E00
         vg[i, :, L:] = 0x7E00
     scale = 1.0 / math.sqrt(hd)
-    got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, kv_len=lens, kv_override=(kg, vg))
+    got = run_gqa(c, n_head, n_kvh, n_tok, n_kv, hd, scale, flags=variant, kv_len=lens,
+                  kv_override=(kg, vg))
     want = oracle_gqa(oracle_mod, dict(c, mask=mask), n_head, n_kvh, n_tok, n_kv, hd, scale,
                       oracle_mod.Q_F32)
     assert_close(got, want, "hd80 kv_len")
