@@ -166,18 +166,19 @@ def test_device_valid_key_counts(oracle_mod, shape, variant):
             assert np.array_equal(got[i], np.zeros_like(got[i])), f"instance {i}"
 
 
-def test_graph_replays_follow_device_key_counts():
+@pytest.mark.parametrize("variant", [FUSED, DECOMP], ids=["fused", "decomposed"])
+def test_graph_replays_follow_device_key_counts(variant):
     """One graph captured with a device key-count array; between replays the
     host writes new counts, and every replay equals an eager call with them."""
     import gqa_decode_attention_fr_amd as F
     n_inst, n_head, n_kvh, n_tok, n_kv, hd = 3, 16, 4, 4, 2048, 128
-    say("graph replays with changing kv_len")
+    say(f"graph replays with changing kv_len, variant={variant}")
     c = W.random_case(801, n_head, n_tok, n_kv, hd, mask_kind="none", n_inst=n_inst,
                       n_kv_head=n_kvh)
     scale = 1.0 / math.sqrt(hd)
     M = n_head * n_tok
     units, grp = n_inst * n_kvh, n_head // n_kvh
-    F.fr_decode_attn_reserve(units, grp, n_tok, n_kv, hd)
+    F.fr_decode_attn_reserve(units, grp, n_tok, n_kv, hd, variant)
     q, k, v = dev(c["q"], torch), dev(c["k"], torch), dev(c["v"], torch)
     lens = torch.full((n_inst,), n_kv, dtype=torch.int32, device="cuda")
     out = torch.zeros((n_inst, n_tok, n_head, hd), dtype=torch.float32, device="cuda")
@@ -185,7 +186,7 @@ def test_graph_replays_follow_device_key_counts():
     def call():
         F.fr_decode_attn_gqa(q, F.FR_Q_F32, k, v, None, out, n_inst, M * hd,
                              n_kvh * n_kv * hd, 0, M * hd, n_head, n_kvh, n_kv * hd, n_tok,
-                             n_kv, hd, scale, kv_len=lens)
+                             n_kv, hd, scale, variant, kv_len=lens)
 
     call()
     torch.cuda.synchronize()
