@@ -363,3 +363,40 @@ def test_binding_constants_match_the_header():
     for n in mirrored:
         assert n in both, n
         assert getattr(B, n) == both[n], n
+
+
+def test_plan_invariants_over_random_shapes():
+    """Seeded random shapes, masked and unmasked plans of the fused variant:
+    every key and row is covered with no empty split, the grid is what the
+    plan says, the wave rules hold, and the default workspace size covers
+    both plans' partials."""
+    import numpy as np
+    rng = np.random.default_rng(77)
+    for _ in range(600):
+        n_inst = int(rng.integers(1, 65))
+        n_head = int(rng.integers(1, 129))
+        unmasked = bool(rng.random() < 0.5)
+        n_tok = int(rng.integers(1, 4097 if unmasked else 65))
+        n_kv = int(rng.integers(1, 100_001))
+        hd = int(rng.choice([64, 80, 128, 256]))
+        if n_inst * n_head * n_tok > (1 << 24):
+            continue
+        shape = (n_inst, n_head, n_tok, n_kv, hd)
+        flags = B.FR_PLAN_UNMASKED if unmasked else 0
+        p = B.fr_decode_attn_plan(*shape, flags)
+        M = n_head * n_tok
+        tiles_total = -(-M // 16)
+        assert p["variant"] == 1 and p["tiles"] == 1 and p["waves"] in (4, 8), shape
+        assert p["chunk"] % 64 == 0, shape
+        assert p["n_split"] * p["chunk"] >= n_kv > (p["n_split"] - 1) * p["chunk"], shape
+        assert p["n_rowblk"] * p["waves"] * 16 >= M, shape
+        assert (p["n_rowblk"] - 1) * p["waves"] * 16 < M, shape       # no empty row block
+        assert p["grid"] == n_inst * p["n_rowblk"] * p["n_split"], shape
+        assert p["grid"] <= max(256, n_inst * p["n_rowblk"]), shape
+        if not unmasked and n_tok > 16:
+            assert p["waves"] == 8, shape                              # mask rows for 64 tokens
+        if tiles_total <= 16 and n_tok <= 16:
+            assert p["waves"] == 4, shape
+        need = 0 if p["n_split"] == 1 else n_inst * p["n_split"] * M * (hd * 4 + 8)
+        assert B.fr_decode_attn_workspace_size(*shape, flags) >= need, shape
+        assert B.fr_decode_attn_workspace_size(*shape, 0) >= need, shape  # covers both plans
