@@ -7,4 +7,5 @@ from .binding import (  # noqa: F401
     FrError,
     fr_abi_version, fr_decode_attn, fr_decode_attn_batched, fr_decode_attn_ex, fr_decode_attn_gqa,
     fr_decode_attn_plan, fr_decode_attn_profile_events, fr_decode_attn_q16, fr_decode_attn_reserve,
+    fr_decode_attn_workspace_query, fr_decode_attn_workspace_release,
     fr_decode_attn_workspace_size, fr_f16_copy_batch, fr_qkv_post, fr_status_str)

@@ -38,7 +38,8 @@ FR_MAX_COPIES = 4096
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
             "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_workspace_size",
-            "fr_decode_attn_reserve",
+            "fr_decode_attn_reserve", "fr_decode_attn_workspace_query",
+            "fr_decode_attn_workspace_release",
             "fr_decode_attn_plan", "fr_decode_attn_profile_events", "fr_f16_copy_batch",
             "fr_qkv_post",
             "fr_status_str",
@@ -93,6 +94,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                   ctypes.POINTER(i32)]
     lib.fr_decode_attn_workspace_size.restype = sz
     lib.fr_decode_attn_reserve.argtypes = [i32, i32, i32, i32, i32, u32]
+    lib.fr_decode_attn_workspace_query.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz),
+                                                   ctypes.POINTER(i32)]
+    lib.fr_decode_attn_workspace_query.restype = i32
+    lib.fr_decode_attn_workspace_release.argtypes = []
+    lib.fr_decode_attn_workspace_release.restype = i32
     lib.fr_decode_attn_plan.argtypes = [i32, i32, i32, i32, i32, u32, ctypes.POINTER(i32), i32]
     lib.fr_qkv_post.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32,
                                 i32, i32, i32, f32, f32, vp]
@@ -193,6 +199,19 @@ def fr_decode_attn_workspace_size(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> i
 def fr_decode_attn_reserve(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> None:
     _check(load().fr_decode_attn_reserve(n_inst, n_head, n_tok, n_kv, hd, flags),
            "fr_decode_attn_reserve")
+
+
+def fr_decode_attn_workspace_query() -> tuple[int, int, int]:
+    """(address, bytes, retired buffers) of the current device's library workspace."""
+    p, n, r = ctypes.c_void_p(), ctypes.c_size_t(), ctypes.c_int()
+    _check(load().fr_decode_attn_workspace_query(ctypes.byref(p), ctypes.byref(n),
+                                                 ctypes.byref(r)),
+           "fr_decode_attn_workspace_query")
+    return int(p.value or 0), int(n.value), int(r.value)
+
+
+def fr_decode_attn_workspace_release() -> None:
+    _check(load().fr_decode_attn_workspace_release(), "fr_decode_attn_workspace_release")
 
 
 def fr_decode_attn_plan(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> dict:

@@ -127,10 +127,16 @@ int validate(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
   return FR_OK;
 }
 
-// ---- library-owned, per-device, grow-only workspace
+// ---- library-owned, per-device, grow-only workspace.  A buffer that is
+// replaced by a larger one is retired, never freed while the process runs: a
+// graph captured earlier keeps its address in its kernel arguments and may be
+// replayed at any time (the grow-only, address-stable slots that the
+// FlashRT-llama.cpp development guide asks of caches, section "Caches (all
+// capture-safe)").  Only fr_decode_attn_workspace_release frees them.
 struct DeviceWs {
   void *ptr = nullptr;
   size_t bytes = 0;
+  std::vector<void *> retired;   // earlier, smaller buffers (still valid memory)
 };
 std::mutex g_ws_mu;
 std::vector<DeviceWs> g_ws;
@@ -141,7 +147,8 @@ size_t round_ws(size_t need) {
 }
 
 // Returns a workspace of at least `need` bytes on the current device.  Grows
-// only outside graph capture (FR_ERR_CAPTURE otherwise).
+// only outside graph capture (FR_ERR_CAPTURE otherwise).  A new buffer is
+// zero-filled before it is handed out (synchronously, outside any capture).
 int library_ws(size_t need, hipStream_t stream, bool check_capture, void **out) {
   *out = nullptr;
   if (need == 0) return FR_OK;
@@ -159,20 +166,36 @@ int library_ws(size_t need, hipStream_t stream, bool check_capture, void **out) 
     if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return FR_ERR_HIP;
     if (cs != hipStreamCaptureStatusNone) return FR_ERR_CAPTURE;
   }
-  if (w.ptr) {
-    // earlier calls may still be reading the old buffer
-    if (hipDeviceSynchronize() != hipSuccess) return FR_ERR_HIP;
-    if (hipFree(w.ptr) != hipSuccess) return FR_ERR_HIP;
-    w.ptr = nullptr;
-    w.bytes = 0;
-  }
   const size_t bytes = round_ws(need);
   void *p = nullptr;
   if (hipMalloc(&p, bytes) != hipSuccess) return FR_ERR_HIP;
+  if (hipMemset(p, 0, bytes) != hipSuccess) {
+    (void)hipFree(p);
+    return FR_ERR_HIP;
+  }
+  if (w.ptr) w.retired.push_back(w.ptr);   // earlier calls and graphs may still use it
   w.ptr = p;
   w.bytes = bytes;
   *out = p;
   return FR_OK;
+}
+
+// Frees every library workspace buffer of the current device (current and
+// retired) after a device synchronisation.
+int release_library_ws() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if ((int)g_ws.size() <= dev) return FR_OK;
+  DeviceWs &w = g_ws[dev];
+  if (!w.ptr && w.retired.empty()) return FR_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return FR_ERR_HIP;
+  int st = FR_OK;
+  for (void *p : w.retired)
+    if (hipFree(p) != hipSuccess) st = FR_ERR_HIP;
+  if (w.ptr && hipFree(w.ptr) != hipSuccess) st = FR_ERR_HIP;
+  w = DeviceWs{};
+  return st;
 }
 
 int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const uint16_t *mask,
@@ -192,10 +215,28 @@ int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const
   Plan plan;
   st = fr::make_plan(n_inst * n_kvh, n_head / n_kvh, n_tok, n_kv, hd, flags, &plan);
   if (st != FR_OK) return st;
+  // Memory the kernels write (out, and a caller workspace) must not overlap
+  // anything they read: q, k, v, the mask and the valid key counts (the
+  // library's own workspace is disjoint from every caller buffer).
+  const int64_t M = (int64_t)n_head * n_tok;
+  const int64_t kv_elems = (int64_t)(n_kvh - 1) * kvh_stride + (int64_t)n_kv * hd;
+  const Range r_out = span(out, n_inst, out_stride, M * hd, 4);
+  const Range r_len = kv_len ? span(kv_len, 1, 0, n_inst, 4) : Range{0, 0};
+  if (kv_len && overlaps(r_len, r_out)) return FR_ERR_INVALID;
   if (caller_ws) {
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
       return FR_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 256)) return FR_ERR_INVALID;
+    if (plan.ws_bytes > 0) {
+      const Range r_ws = span(workspace, 1, 0, (int64_t)plan.ws_bytes, 1);
+      const size_t qsize = q_format == FR_Q_F16 ? 2 : 4;
+      if (overlaps(r_ws, r_out) || overlaps(r_ws, span(q, n_inst, q_stride, M * hd, qsize)) ||
+          overlaps(r_ws, span(k, n_inst, kv_stride, kv_elems, 2)) ||
+          overlaps(r_ws, span(v, n_inst, kv_stride, kv_elems, 2)) ||
+          (mask && overlaps(r_ws, span(mask, n_inst, mask_stride, (int64_t)n_tok * n_kv, 2))) ||
+          (kv_len && overlaps(r_ws, r_len)))
+        return FR_ERR_INVALID;
+    }
   } else {
     st = library_ws(plan.ws_bytes, (hipStream_t)stream, true, &workspace);
     if (st != FR_OK) return st;
@@ -308,6 +349,22 @@ int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
   void *p = nullptr;
   return library_ws(need, nullptr, false, &p);
 }
+
+int fr_decode_attn_workspace_query(void **ptr, size_t *bytes, int *n_retired) {
+  if (ptr) *ptr = nullptr;
+  if (bytes) *bytes = 0;
+  if (n_retired) *n_retired = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if ((int)g_ws.size() <= dev) return FR_OK;
+  if (ptr) *ptr = g_ws[dev].ptr;
+  if (bytes) *bytes = g_ws[dev].bytes;
+  if (n_retired) *n_retired = (int)g_ws[dev].retired.size();
+  return FR_OK;
+}
+
+int fr_decode_attn_workspace_release(void) { return release_library_ws(); }
 
 int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flags,
                         int *info, int n_info) {

@@ -66,7 +66,9 @@
  * (the capture-safety rule of the FlashRT-llama.cpp development guide,
  * section "Caches (all capture-safe)"): a call that would need to grow it
  * during capture returns FR_ERR_CAPTURE; call fr_decode_attn_reserve before
- * capturing.  Calls that share the library workspace must be ordered on one
+ * capturing.  A buffer outgrown by a later call is kept, not freed, so graphs
+ * captured with it stay valid; fr_decode_attn_workspace_release frees them
+ * all.  Calls that share the library workspace must be ordered on one
  * stream (or otherwise serialised); concurrent calls on different streams of
  * one device must each pass their own workspace to fr_decode_attn_ex (or
  * fr_decode_attn_gqa).
@@ -137,7 +139,10 @@ int fr_decode_attn_q16(const uint16_t *q16, const uint16_t *k, const uint16_t *v
 
 /*
  * n_inst independent instances (e.g. the layers of one model step) in one
- * launch sequence.  Instance i reads q + i*q_stride, k + i*kv_stride,
+ * launch sequence.  The pages run the window once per layer inside the model
+ * graph and define no batched call; it is this library's, for the pi0.5
+ * action step of 18 layer instances (one launch sequence instead of 18, each
+ * instance computed exactly as fr_decode_attn would).  Instance i reads q + i*q_stride, k + i*kv_stride,
  * v + i*kv_stride, mask + i*mask_stride and writes out + i*out_stride; strides
  * count ELEMENTS of each tensor's type.  q_stride and kv_stride may be 0
  * (shared input); mask_stride may be 0 (one mask for all); out_stride must be
@@ -152,7 +157,13 @@ int fr_decode_attn_batched(const void *q, int q_format, const uint16_t *k,
 
 /*
  * Everything: batched instances, flags (FR_Q_ROUND_F16, FR_VARIANT_*), and an
- * optional caller-owned device workspace.  workspace == NULL uses the library
+ * optional caller-owned device workspace.  The pages define no such call; its
+ * options come from them: FR_Q_ROUND_F16 is the single f16 rounding of the
+ * gather that the qkv_post handoff commit of FlashRT PR #185 replaces,
+ * FR_VARIANT_DECOMPOSED the separate QK^T, softmax and PV launches of its
+ * decomposed decode attention commit, and the caller workspace serves the
+ * development guide's "Caches (all capture-safe)" rule for callers that own
+ * their memory.  workspace == NULL uses the library
  * workspace (grow-only, see above); otherwise it must be 256-byte aligned and
  * at least fr_decode_attn_workspace_size(...) bytes, else FR_ERR_WORKSPACE.
  * The library keeps no reference to a caller workspace after the call's
@@ -211,6 +222,9 @@ int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k,
 
 /* Device workspace bytes a call with these sizes and flags needs (0 if none),
  * or 0 with *status set when the sizes are rejected (status may be NULL).
+ * Not defined by the pages: it lets a caller size a workspace before capture,
+ * as the development guide's "Caches (all capture-safe)" section requires of
+ * anything allocated for a captured window.
  * The size does not depend on the query format, so it also suits
  * fr_decode_attn_q16 and FR_Q_F16 calls.  Without FR_PLAN_UNMASKED it covers
  * calls with and without a mask (the plan of an unmasked call with many rows
@@ -220,14 +234,34 @@ size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv
 
 /* Grow the library workspace of the CURRENT device so that calls up to these
  * sizes never allocate.  Synchronous; must not be called during capture.
+ * A buffer replaced by a larger one is retired, not freed: graphs captured
+ * with it keep working until fr_decode_attn_workspace_release.  The pages
+ * define no such call; it serves the capture-safety rule above (the
+ * development guide's "Caches (all capture-safe)": reserve before capture).
  * Returns FR_OK or a negative fr_status. */
 int fr_decode_attn_reserve(int n_inst, int n_head, int n_tok, int n_kv, int hd,
                            unsigned flags);
 
+/* The library workspace of the CURRENT device: its address (NULL if none yet),
+ * its size in bytes and how many smaller, retired buffers the library still
+ * holds for graphs captured with them.  Any output pointer may be NULL.  A
+ * diagnostic the pages do not define (it lets a caller check that a captured
+ * graph's workspace is still allocated).  Returns FR_OK or FR_ERR_HIP. */
+int fr_decode_attn_workspace_query(void **ptr, size_t *bytes, int *n_retired);
+
+/* Frees every library workspace buffer of the CURRENT device, current and
+ * retired, after synchronising the device.  Graphs captured with any of them
+ * must not be replayed afterwards; the next call allocates afresh.  Not during
+ * capture.  Not defined by the pages (the counterpart of the grow-only rule
+ * above, for a caller that is done with the library).  Returns FR_OK or
+ * FR_ERR_HIP. */
+int fr_decode_attn_workspace_release(void);
+
 /*
  * The launch plan a call with these sizes and flags would use (the same for
  * every query format; pass FR_PLAN_UNMASKED for a call with mask == NULL),
- * for tests and benchmarks.  Fills up to n_info ints of
+ * for tests and benchmarks.  Not defined by the pages (a diagnostic of how
+ * this library splits the work).  Fills up to n_info ints of
  * info[]:
  *   [0] variant (1 fused, 2 decomposed)  [1] key splits per instance
  *   [2] keys per split                   [3] waves per workgroup
@@ -239,11 +273,13 @@ int fr_decode_attn_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd,
                         unsigned flags, int *info, int n_info);
 
 /*
- * Optional kernel timing.  When start and stop are both non-NULL (caller-owned
- * hipEvent_t handles passed as void*), every later call on this process
- * records `start` on its stream immediately before its main kernel and `stop`
- * immediately after it: the split kernel of the fused variant, or the whole
- * three- or four-launch sequence of the decomposed one.  hipEventElapsedTime
+ * Optional kernel timing (not defined by the pages: a measurement aid for the
+ * per-call device time and HBM rate of each workload).  When start and stop
+ * are both non-NULL (caller-owned hipEvent_t handles passed as void*), every
+ * later call on this process records `start` on its stream immediately
+ * before its main kernel and `stop` immediately after it: the split kernel of
+ * the fused variant, or the whole three- or four-launch sequence of the
+ * decomposed one.  hipEventElapsedTime
  * on the pair then gives that kernel's device time.  Pass NULL, NULL to stop.
  * The setting is process-wide; calls on several host threads share it.
  * Returns FR_OK, or FR_ERR_INVALID if exactly one event is NULL.
@@ -313,10 +349,13 @@ typedef struct fr_f16_copy {
 #define FR_MAX_COPIES 4096
 int fr_f16_copy_batch(const fr_f16_copy *copies, int n_copies, void *stream);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code.  Not defined by the pages; it
+ * names why a call was declined (the development guide's "Adding a fusion
+ * window" predicate declines shapes it does not pin, and the caller falls back). */
 const char *fr_status_str(int status);
 
-/* ABI version of this header (bumped on incompatible changes). */
+/* ABI version of this header (bumped on incompatible changes).  Not defined by
+ * the pages. */
 #define FR_DECODE_ATTN_ABI_VERSION 1
 int fr_abi_version(void);
 

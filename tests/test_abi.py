@@ -93,6 +93,13 @@ def call(**kw):
     (dict(n_inst=2, os_=8 * 10 * 256, kvs=5), B.FR_ERR_INVALID),  # kv stride breaks alignment
     (dict(n_inst=2, os_=8 * 10 * 256, ms=-1), B.FR_ERR_INVALID),
     (dict(ws=0x900000, ws_bytes=16), B.FR_ERR_WORKSPACE),  # caller workspace too small
+    # a caller workspace the kernels would write over an input or the output
+    # (the plan's workspace here is about 1.3 MB: each range below starts in or
+    # just before the named tensor)
+    (dict(ws=Q, ws_bytes=1 << 24), B.FR_ERR_INVALID),            # from q on
+    (dict(ws=0x280000, ws_bytes=1 << 24), B.FR_ERR_INVALID),     # from v on (k ends there)
+    (dict(ws=0x3F0000, ws_bytes=1 << 24), B.FR_ERR_INVALID),     # from the mask on
+    (dict(ws=0x4FFF00, ws_bytes=1 << 24), B.FR_ERR_INVALID),     # over out
 ])
 def test_rejected_before_any_launch(kw, status):
     assert call(**kw) == status
@@ -122,6 +129,9 @@ def gqa_call(**kw):
     (dict(n_tok=65), B.FR_ERR_UNSUPPORTED),
     (dict(q=None), B.FR_ERR_INVALID),
     (dict(kvl=0x600002), B.FR_ERR_INVALID),                  # misaligned key counts
+    (dict(kvl=OUT + 64), B.FR_ERR_INVALID),                  # key counts inside out
+    (dict(kvl=0x900100, ws=0x900000, ws_bytes=1 << 20), B.FR_ERR_INVALID),  # ... in the workspace
+    (dict(ws=K + 0x40000, ws_bytes=1 << 20), B.FR_ERR_INVALID),  # workspace over k
 ])
 def test_gqa_rejected_before_any_launch(kw, status):
     assert gqa_call(**kw) == status

@@ -373,3 +373,74 @@ def test_capture_refuses_to_grow_workspace():
                 status = e.status
     torch.cuda.synchronize()
     assert status == F.FR_ERR_CAPTURE
+
+
+def _hip_alloc_range(ptr: int):
+    """(base, size) of the live device allocation holding ptr, or None when no
+    allocation holds it (hipMemGetAddressRange of the HIP runtime torch loaded)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    base, size = ctypes.c_void_p(), ctypes.c_size_t()
+    st = hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), ctypes.c_void_p(ptr))
+    return (int(base.value or 0), int(size.value)) if st == 0 else None
+
+
+def test_graph_survives_workspace_growth():
+    """A graph captured after a reserve keeps working after a larger eager call
+    has grown the library workspace: the outgrown buffer is retired, not freed
+    (FlashRT-llama.cpp development guide, 'Caches (all capture-safe)')."""
+    import gqa_decode_attention_fr_amd as F
+    say("graph across workspace growth")
+    torch.cuda.synchronize()
+    F.fr_decode_attn_workspace_release()
+    assert F.fr_decode_attn_workspace_query() == (0, 0, 0)
+    w = W.H16_HD128_Q16
+    g = W.generate(w)
+    F.fr_decode_attn_reserve(1, w.n_head, w.n_tok, w.n_kv, w.hd)
+    p0, n0, r0 = F.fr_decode_attn_workspace_query()
+    assert p0 != 0 and n0 >= F.fr_decode_attn_workspace_size(1, w.n_head, w.n_tok, w.n_kv, w.hd)
+    assert r0 == 0
+    q, k, v, m = (dev(g[x][0], torch) for x in ("q", "k", "v", "mask"))
+    out = torch.zeros((w.n_tok, w.n_head, w.hd), dtype=torch.float32, device="cuda")
+
+    def call():
+        F.fr_decode_attn_q16(q, k, v, m, out, w.n_head, w.n_tok, w.n_kv, w.hd, w.scale)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    # an eager call with a larger workspace grows the library's buffer
+    big = dict(n_head=32, n_tok=16, n_kv=32768, hd=128)
+    need_big = F.fr_decode_attn_workspace_size(1, *big.values())
+    assert need_big > n0
+    bq = torch.zeros((big["n_tok"], big["n_head"], big["hd"]), dtype=torch.float32, device="cuda")
+    bk = torch.zeros((big["n_kv"], big["hd"]), dtype=torch.float16, device="cuda")
+    bo = torch.empty_like(bq)
+    F.fr_decode_attn(bq, bk, bk, None, bo, big["n_head"], big["n_tok"], big["n_kv"], big["hd"],
+                     0.088)
+    torch.cuda.synchronize()
+    p1, n1, r1 = F.fr_decode_attn_workspace_query()
+    assert p1 != p0 and n1 >= need_big and r1 == 1
+    # the retired buffer is still a live allocation of its full size
+    rng = _hip_alloc_range(p0)
+    assert rng is not None and rng[0] == p0 and rng[1] >= n0
+    # fresh allocations in between may take any freed memory
+    junk = [torch.full((4 << 20,), float("nan"), device="cuda") for _ in range(8)]
+    for it in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {it} after growth"
+        call()   # eager work between replays (uses the grown buffer)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    del junk, graph

@@ -440,3 +440,28 @@ def test_rope_scores_depend_only_on_relative_position(oracle_mod):
     h = hd // 2
     np.testing.assert_allclose(q0[..., :h] ** 2 + q0[..., h:] ** 2,
                                x[..., :h] ** 2 + x[..., h:] ** 2, rtol=1e-12)
+
+
+def _closed_form(expr: str) -> float:
+    """Evaluates a hand-derived closed form: numbers, + - * and cos/sin only."""
+    import re
+    assert re.fullmatch(r"[0-9.\s+\-*()cosin]*", expr), expr
+    return float(eval(expr, {"__builtins__": {}}, {"cos": math.cos, "sin": math.sin}))
+
+
+def test_rope_hand_derived_cases(oracle_mod):
+    """The RoPE frequency schedule and the NeoX pairing against hand-derived
+    closed forms (tests/golden/rope_neox_cases.json): exact angles at small
+    positions, each output a cos/sin expression written from the definition."""
+    with open(os.path.join(HERE, "golden", "rope_neox_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        qkv = np.array(c["qkv"], dtype=np.float32)
+        q, k, v = oracle_mod.qkv_post(qkv, np.array(c["pos"], dtype=np.int32), c["n_head"],
+                                      c["n_kv_head"], c["n_tok"], c["hd"], c["base"],
+                                      c["q_scale"])
+        for name, got in (("q", q), ("k", k), ("v", v)):
+            want = np.vectorize(_closed_form, otypes=[np.float64])(np.array(c[name], dtype=object))
+            np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15,
+                                       err_msg=f"{c['name']} {name}")
+
