@@ -34,10 +34,12 @@ FR_MAX_TOKENS = 64
 FR_MAX_TOKENS_UNMASKED = 16384
 FR_MAX_HEADS = 1024
 FR_MAX_COPIES = 4096
+FR_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol the header declares (checked by the ABI tests).
 EXPORTED = ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
-            "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_workspace_size",
+            "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_gqa_noalloc",
+            "fr_decode_attn_workspace_size",
             "fr_decode_attn_reserve", "fr_decode_attn_workspace_query",
             "fr_decode_attn_workspace_release",
             "fr_decode_attn_plan", "fr_decode_attn_profile_events", "fr_f16_copy_batch",
@@ -85,8 +87,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fr_decode_attn_ex.argtypes = batched + [u32, vp, sz, vp]
     lib.fr_decode_attn_gqa.argtypes = (batched[:5] + [vp] + batched[5:12] + [i32, i64] +
                                        batched[12:] + [u32, vp, sz, vp])
+    lib.fr_decode_attn_gqa_noalloc.argtypes = (batched[:5] + [vp] + batched[5:12] + [i32, i64] +
+                                               batched[12:] + [u32, vp])
     for fn in ("fr_decode_attn", "fr_decode_attn_q16", "fr_decode_attn_batched",
-               "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_reserve",
+               "fr_decode_attn_ex", "fr_decode_attn_gqa", "fr_decode_attn_gqa_noalloc",
+               "fr_decode_attn_reserve",
                "fr_decode_attn_plan",
                "fr_abi_version"):
         getattr(lib, fn).restype = i32
@@ -186,6 +191,19 @@ def fr_decode_attn_gqa(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride
                                      out_stride, n_head, n_kv_head, kv_head_stride, n_tok, n_kv,
                                      hd, scale, flags, _ptr(workspace), workspace_bytes,
                                      _stream(stream)), "fr_decode_attn_gqa")
+
+
+def fr_decode_attn_gqa_noalloc(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride,
+                               mask_stride, out_stride, n_head, n_kv_head, kv_head_stride, n_tok,
+                               n_kv, hd, scale, flags=0, stream=None, kv_len=None) -> None:
+    """fr_decode_attn_gqa without a workspace: partials in the library's fixed
+    device array (FR_NOALLOC_SCRATCH_BYTES); no allocation of any kind."""
+    _check(load().fr_decode_attn_gqa_noalloc(_ptr(q), q_format, _ptr(k), _ptr(v), _ptr(mask),
+                                             _ptr(kv_len), _ptr(out), n_inst, q_stride,
+                                             kv_stride, mask_stride, out_stride, n_head,
+                                             n_kv_head, kv_head_stride, n_tok, n_kv, hd, scale,
+                                             flags, _stream(stream)),
+           "fr_decode_attn_gqa_noalloc")
 
 
 def fr_decode_attn_workspace_size(n_inst, n_head, n_tok, n_kv, hd, flags=0) -> int:

@@ -198,6 +198,30 @@ int release_library_ws() {
   return st;
 }
 
+// ---- the fixed scratch array of fr_decode_attn_gqa_noalloc.  In host code
+// `scratch` names a host-side stand-in, not device memory: kernels get the
+// per-device address that hipGetSymbolAddress reports, never the name itself.
+static __device__ __align__(256) unsigned char scratch[FR_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;   // per device; null until looked up
+
+// The current device's address of `scratch` (looked up once per device, with
+// that device current).  FR_ERR_HIP if the lookup fails.
+int scratch_address(void **out) {
+  *out = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FR_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FR_OK;
+}
+
 int run(const void *q, int q_format, const uint16_t *k, const uint16_t *v, const uint16_t *mask,
         const int32_t *kv_len, float *out, int n_inst, int64_t q_stride, int64_t kv_stride, int64_t mask_stride,
         int64_t out_stride, int n_head, int n_kvh, int64_t kvh_stride, int n_tok, int n_kv,
@@ -319,6 +343,38 @@ int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k, const uin
   return run(q, q_format, k, v, mask, kv_len, out, n_inst, q_stride, kv_stride, mask_stride,
              out_stride, n_head, n_kv_head, kv_head_stride, n_tok, n_kv, hd, scale, flags, workspace,
              workspace_bytes, workspace != nullptr, stream);
+}
+
+int fr_decode_attn_gqa_noalloc(const void *q, int q_format, const uint16_t *k, const uint16_t *v,
+                               const uint16_t *mask, const int32_t *kv_len, float *out,
+                               int n_inst, int64_t q_stride, int64_t kv_stride,
+                               int64_t mask_stride, int64_t out_stride, int n_head,
+                               int n_kv_head, int64_t kv_head_stride, int n_tok, int n_kv,
+                               int hd, float scale, unsigned flags, void *stream) {
+  // The plan's workspace must fit the fixed array: checked here (after the
+  // same argument checks the other entry points make) so that the address
+  // lookup below is the only HIP call before the launch.
+  int st = validate(q, q_format, k, v, mask, out, n_inst, q_stride, kv_stride, mask_stride,
+                    out_stride, n_head, n_kv_head, kv_head_stride, n_tok, n_kv, hd, scale, flags);
+  if (st != FR_OK) return st;
+  if (kv_len) {
+    if (!aligned(kv_len, 4)) return FR_ERR_INVALID;
+    const int64_t os = n_inst > 1 ? out_stride : 0;
+    if (overlaps(span(kv_len, 1, 0, n_inst, 4),
+                 span(out, n_inst, os, (int64_t)n_head * n_tok * hd, 4)))
+      return FR_ERR_INVALID;
+  }
+  const unsigned pflags = (flags & ~FR_PLAN_UNMASKED) | (mask ? 0u : FR_PLAN_UNMASKED);
+  Plan plan;
+  st = fr::make_plan(n_inst * n_kv_head, n_head / n_kv_head, n_tok, n_kv, hd, pflags, &plan);
+  if (st != FR_OK) return st;
+  if (plan.ws_bytes > (size_t)FR_NOALLOC_SCRATCH_BYTES) return FR_ERR_WORKSPACE;
+  void *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != FR_OK) return st;
+  return run(q, q_format, k, v, mask, kv_len, out, n_inst, q_stride, kv_stride, mask_stride,
+             out_stride, n_head, n_kv_head, kv_head_stride, n_tok, n_kv, hd, scale, flags, ws,
+             (size_t)FR_NOALLOC_SCRATCH_BYTES, true, stream);
 }
 
 size_t fr_decode_attn_workspace_size(int n_inst, int n_head, int n_tok, int n_kv, int hd,

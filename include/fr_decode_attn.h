@@ -91,7 +91,8 @@ typedef enum fr_status {
                                 n_head above 1024, n_kv above 2^26 or n_tok*n_kv above 2^30 */
     FR_ERR_CAPTURE = -3,     /* the library workspace would have to grow while the stream is captured */
     FR_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
-    FR_ERR_WORKSPACE = -5    /* the caller's workspace is smaller than fr_decode_attn_workspace_size */
+    FR_ERR_WORKSPACE = -5    /* the caller's workspace is smaller than fr_decode_attn_workspace_size
+                                (fr_decode_attn_gqa_noalloc: its fixed array is) */
 } fr_status;
 
 /* Query formats for fr_decode_attn_batched / fr_decode_attn_ex. */
@@ -219,6 +220,31 @@ int fr_decode_attn_gqa(const void *q, int q_format, const uint16_t *k,
                        int n_kv_head, int64_t kv_head_stride, int n_tok, int n_kv,
                        int hd, float scale, unsigned flags, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * fr_decode_attn_gqa for callers that cannot allocate device memory (code
+ * under graph capture without a prior reserve, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without a workspace.  The split
+ * partials go to a fixed device array inside the library of
+ * FR_NOALLOC_SCRATCH_BYTES bytes (one per GPU the library runs on, held until
+ * the process ends); the call makes no allocation of any kind.  A call whose
+ * plan needs more than that (fr_decode_attn_workspace_size) returns
+ * FR_ERR_WORKSPACE and launches nothing.  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents: calls that overlap in
+ * time on one GPU (different streams, or host threads racing) corrupt each
+ * other's partials, so they must be ordered.  No part of the array needs to
+ * start at zero: each call writes every partial it reads.  Otherwise as
+ * fr_decode_attn_gqa.
+ */
+#define FR_NOALLOC_SCRATCH_BYTES 33554432u /* 32 MiB */
+int fr_decode_attn_gqa_noalloc(const void *q, int q_format, const uint16_t *k,
+                               const uint16_t *v, const uint16_t *mask,
+                               const int32_t *kv_len, float *out,
+                               int n_inst, int64_t q_stride, int64_t kv_stride,
+                               int64_t mask_stride, int64_t out_stride, int n_head,
+                               int n_kv_head, int64_t kv_head_stride, int n_tok,
+                               int n_kv, int hd, float scale, unsigned flags,
+                               void *stream);
 
 /* Device workspace bytes a call with these sizes and flags needs (0 if none),
  * or 0 with *status set when the sizes are rejected (status may be NULL).

@@ -137,6 +137,43 @@ def test_gqa_rejected_before_any_launch(kw, status):
     assert gqa_call(**kw) == status
 
 
+def noalloc_call(**kw):
+    a = dict(q=Q, fmt=B.FR_Q_F32, k=K, v=V, mask=MASK, out=OUT, n_inst=1, qs=0, kvs=0, ms=0,
+             os_=0, n_head=8, n_kvh=1, kvhs=0, n_tok=10, n_kv=1024, hd=256, scale=0.0625,
+             flags=0, kvl=None)
+    a.update(kw)
+    return B.load().fr_decode_attn_gqa_noalloc(a["q"], a["fmt"], a["k"], a["v"], a["mask"],
+                                               a["kvl"], a["out"], a["n_inst"], a["qs"],
+                                               a["kvs"], a["ms"], a["os_"], a["n_head"],
+                                               a["n_kvh"], a["kvhs"], a["n_tok"], a["n_kv"],
+                                               a["hd"], a["scale"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.FR_ERR_INVALID),
+    (dict(out=Q), B.FR_ERR_INVALID),
+    (dict(n_tok=65), B.FR_ERR_UNSUPPORTED),
+    (dict(n_kvh=3), B.FR_ERR_INVALID),
+    (dict(flags=0x80), B.FR_ERR_INVALID),
+    (dict(kvl=OUT), B.FR_ERR_INVALID),
+    # plans whose partials exceed the fixed 32 MiB array: declined before any HIP call
+    # (fake addresses 1 GiB apart: these tensors are large)
+    (dict(q=1 << 30, k=2 << 30, v=3 << 30, out=4 << 30, mask=None, n_head=32, n_tok=16,
+          n_kv=1 << 20, hd=128, flags=B.FR_VARIANT_DECOMPOSED), B.FR_ERR_WORKSPACE),
+    (dict(q=1 << 30, k=2 << 30, v=3 << 30, out=4 << 30, mask=None, n_head=64, n_tok=16,
+          n_kv=65536, hd=256), B.FR_ERR_WORKSPACE),
+])
+def test_noalloc_rejected_before_any_launch(kw, status):
+    assert noalloc_call(**kw) == status
+
+
+def test_noalloc_limit_matches_workspace_sizes():
+    """The workloads this library measures all fit the fixed array."""
+    for shape in [(18, 8, 10, 1024, 256), (1, 16, 16, 4096, 128), (1, 8, 16, 2048, 256),
+                  (1, 32, 16, 32768, 128), (64, 4, 4, 4096, 128)]:
+        assert B.fr_decode_attn_workspace_size(*shape) <= B.FR_NOALLOC_SCRATCH_BYTES, shape
+
+
 def test_gqa_with_one_kv_head_validates_like_ex():
     # one KV head ignores the head stride; the rest of the checks are shared
     for kw in (dict(n_tok=65), dict(hd=96), dict(out=Q), dict(scale=float("nan"))):
