@@ -75,6 +75,8 @@ def parse_args(argv=None):
                     help="also time a batch as back-to-back single-instance calls (a second "
                          "grid of the same kernels, so kept out of default runs)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the machine probes (launch floor, read rates, merge A/B)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run --steps plain 256 MiB device copies (the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes)")
@@ -285,10 +287,10 @@ def achievable_read_gbps(torch, reps=20):
     return gbps
 
 
-def traffic_for(w_name: str, variant=None):
-    """HBM bytes per main-kernel launch from the committed rocprofv3 counter
-    summary, or None if missing, taken on different kernel sources or (for
-    attention workloads) with another variant."""
+def traffic_record(w_name: str, variant=None):
+    """The committed rocprofv3 counter record of a workload, or None if missing,
+    taken on different kernel sources or (for attention workloads) with another
+    variant."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -299,7 +301,23 @@ def traffic_for(w_name: str, variant=None):
     rec = t.get("workloads", {}).get(w_name)
     if not rec or rec.get("variant") != variant:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def traffic_for(w_name: str, variant=None):
+    """HBM bytes per main-kernel launch from the committed counters (or None)."""
+    rec = traffic_record(w_name, variant)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def call_traffic_for(w_name: str, variant=None):
+    """HBM bytes per call: the main kernel's plus, where the call has one, the
+    combine kernel's (or None)."""
+    rec = traffic_record(w_name, variant)
+    if rec is None or rec.get("hbm_bytes_per_launch") is None:
+        return None
+    comb = rec.get("combine_kernel")
+    return rec["hbm_bytes_per_launch"] + (comb["hbm_bytes_per_launch"] if comb else 0)
 
 
 def cpu_baseline(w, g, gpu_out, repeats):
@@ -333,26 +351,175 @@ def cpu_baseline(w, g, gpu_out, repeats):
             "max_abs_vs_gpu": err}
 
 
+PROBE_LIB = os.path.join(ROOT, "gqa_decode_attention_fr_amd", "libfrprobe.so")
+
+
+def machine_probes(torch):
+    """Machine figures behind the design's limits, measured in this run with
+    the committed probe kernels (libfrprobe.so, csrc/fr_probe.hip):
+
+    - the launch floor: microseconds per launch of back-to-back empty kernels
+      queued behind a GPU sleep, eager and replayed from a captured graph;
+    - HBM read rates: one workgroup (one compute unit) streaming 1 MiB it has
+      not touched before (caches scrubbed by a 512 MiB read elsewhere) with
+      32 KiB or 128 KiB of loads in flight, and 256 workgroups streaming 1 MiB
+      each (the whole chip);
+    - merging key-split partials: 256 workgroups in groups of 4 or 8, each
+      reading 64 KiB and writing a 48 KiB partial; the merge as a second
+      launch against one launch whose last-arriving workgroup merges its group
+      (agent-scope acquire/release fences, or device-coherent sc1 accesses),
+      one launch where the last publisher of each column slice merges that
+      slice, and one launch with combine workgroups that wait for their group.
+    """
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.frp_empty.argtypes = [i32, i32, vp]
+    lib.frp_read.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.frp_merge.argtypes = [i32, vp, vp, vp, vp, i32, i32, vp]
+    for f in (lib.frp_empty, lib.frp_read, lib.frp_merge):
+        f.restype = i32
+    grid, pf, wb = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib.frp_merge_sizes(ctypes.byref(grid), ctypes.byref(pf), ctypes.byref(wb))
+    grid, pf, wb = grid.value, pf.value, wb.value
+
+    def ok(st, what):
+        if st != 0:
+            raise RuntimeError(f"probe {what} failed ({st})")
+
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    # launch floor
+    K = 200
+    ok(lib.frp_empty(1, 20, stream), "empty")
+    torch.cuda._sleep(sleep_cycles_for(torch, 5.0))
+    ev0.record()
+    ok(lib.frp_empty(1, K, stream), "empty")
+    ev1.record()
+    torch.cuda.synchronize()
+    res["empty_kernel_us_per_launch_eager"] = round(ev0.elapsed_time(ev1) * 1e3 / K, 3)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            ok(lib.frp_empty(1, K, int(s.cuda_stream)), "empty")
+    torch.cuda.current_stream().wait_stream(s)
+    graph.replay()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(sleep_cycles_for(torch, 5.0))
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    res["empty_kernel_us_per_launch_graph"] = round(ev0.elapsed_time(ev1) * 1e3 / K, 3)
+    del graph
+
+    # HBM read rates: [0, 512 MiB) is the scrub area, reads come from above it
+    mib = 1 << 20
+    buf = torch.zeros(1024 * mib // 4, dtype=torch.float32, device="cuda")
+    times = torch.zeros(2 * 256, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    base = buf.data_ptr()
+
+    def scrub():
+        ok(lib.frp_read(base, 2 * mib, 256, 8, times.data_ptr(), sink.data_ptr(), stream), "read")
+
+    def read(off, per_wg, n_wg, unroll):
+        scrub()
+        ok(lib.frp_read(base + off, per_wg, n_wg, unroll, times.data_ptr(), sink.data_ptr(),
+                        stream), "read")
+        torch.cuda.synchronize()
+        t = times[: 2 * n_wg].cpu().numpy().reshape(n_wg, 2)
+        return per_wg, t   # ticks of 10 ns
+
+    off = 512 * mib
+    for unroll, kib in ((8, 32), (32, 128)):
+        per, t = read(off, mib, 1, unroll)
+        off += mib
+        res[f"read_one_cu_GBps_{kib}KiB_in_flight"] = round(per / ((t[0, 1] - t[0, 0]) * 10.0), 1)
+    per, t = read(off, mib, 256, 8)
+    res["read_chip_256_workgroups_GBps"] = round(256 * per / ((t[:, 1].max() - t[:, 0].min())
+                                                              * 10.0), 1)
+    res["read_chip_per_workgroup_GBps"] = round(float(np.median(per / ((t[:, 1] - t[:, 0])
+                                                                       * 10.0))), 1)
+    del times, sink
+
+    # merging key-split partials: two launches against one
+    part = torch.zeros(grid * pf, dtype=torch.float32, device="cuda")
+    out = torch.zeros(grid * pf, dtype=torch.float32, device="cuda")
+    cnt = torch.zeros(2 * grid, dtype=torch.int32, device="cuda")
+    slot = grid * wb                       # 16 MiB of cold work input per call
+    n_slots = (512 * mib) // slot
+    merge = {}
+    names = {0: "two_launches", 1: "one_launch_fenced", 2: "one_launch_sc1",
+             3: "one_launch_sliced", 4: "one_launch_waiting_combine"}
+    for n_split in (4, 8):
+        for mode in (0, 1, 2, 3, 4):
+            calls = 40
+            for it in range(4):            # warm-up
+                ok(lib.frp_merge(mode, base + 512 * mib + (it % n_slots) * slot, part.data_ptr(),
+                                 cnt.data_ptr(), out.data_ptr(), n_split, it, stream), "merge")
+            torch.cuda.synchronize()
+            torch.cuda._sleep(sleep_cycles_for(torch, 5.0))
+            ev0.record()
+            for it in range(calls):
+                ok(lib.frp_merge(mode, base + 512 * mib + (it % n_slots) * slot, part.data_ptr(),
+                                 cnt.data_ptr(), out.data_ptr(), n_split, it, stream), "merge")
+            ev1.record()
+            torch.cuda.synchronize()
+            got = out[: (grid // n_split) * pf].cpu().numpy().reshape(grid // n_split, pf)
+            it = calls - 1
+            c = np.arange(pf)
+            want = sum(((it * 131 + s_ * 7 + c) % 1021).astype(np.float64) for s_ in range(n_split))
+            correct = bool(np.array_equal(got, np.broadcast_to(want, got.shape)))
+            merge[f"{names[mode]}_groups_of_{n_split}_us"] = round(ev0.elapsed_time(ev1) * 1e3
+                                                                  / calls, 3)
+            if not correct:
+                merge[f"{names[mode]}_groups_of_{n_split}_wrong"] = True
+    res["merge_partials"] = merge
+    del buf, part, out, cnt
+    torch.cuda.empty_cache()
+    return res
+
+
 RIDGE_FLOP_PER_BYTE = PEAK_F16_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # ~312
 
 
-def roofline(w, kern_ms, achieved_gbs, traffic):
-    """The bound of the split kernel from the workload's algorithmic intensity:
-    below the ridge it is HBM bytes per second against 8 TB/s; above it (long
-    context) the two contractions' flops against the dense f16 matrix-core
-    peak.  (An f32 query runs its score contraction twice, hi and lo; those
-    extra flops are not counted: the figure is algorithmic.)"""
-    if w.flops() / w.algorithmic_bytes() <= RIDGE_FLOP_PER_BYTE:
-        return {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
-                "traffic": traffic}
-    tflops = w.flops() / (kern_ms * 1e-3) / 1e12
-    return {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_MFMA_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_MFMA_TFLOPS, 4),
-            "traffic": traffic}
+def roofline(w, kern_ms, achieved_gbs, traffic, ms_call=None, call_traffic=None):
+    """The bound of the split kernel (the dominant kernel) from the workload's
+    algorithmic intensity: below the ridge it is HBM bytes per second against
+    8 TB/s; above it (long context, prefill) the two contractions' flops against
+    the dense f16 matrix-core peak.  (An f32 query runs its score contraction
+    twice, hi and lo; those extra flops are not counted: the figure is
+    algorithmic.)  Beside it, the same figure for the whole call (every launch
+    of it, from the plain-call rate) and the call's counter traffic (split plus
+    combine kernel)."""
+    hbm = w.flops() / w.algorithmic_bytes() <= RIDGE_FLOP_PER_BYTE
+    if hbm:
+        rec = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
+               "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+               "traffic": traffic}
+    else:
+        tflops = w.flops() / (kern_ms * 1e-3) / 1e12
+        rec = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_MFMA_TFLOPS,
+               "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_MFMA_TFLOPS, 4),
+               "traffic": traffic}
+    if ms_call is not None:
+        if hbm:
+            call = w.algorithmic_bytes() / (ms_call * 1e-3) / 1e9
+            rec["call_achieved"] = round(call, 1)
+            rec["call_frac"] = round(call / PEAK_HBM_GBS, 4)
+        else:
+            call = w.flops() / (ms_call * 1e-3) / 1e12
+            rec["call_achieved"] = round(call, 2)
+            rec["call_frac"] = round(call / PEAK_F16_MFMA_TFLOPS, 4)
+        rec["call_traffic"] = call_traffic
+    return rec
 
 
-def run_workload(args, torch, F, W, w):
+def run_workload(args, torch, F, W, w, probes=None):
     flags = {"auto": 0, "fused": F.FR_VARIANT_FUSED,
              "decomposed": F.FR_VARIANT_DECOMPOSED}[args.variant]
     if args.round_f16:
@@ -424,6 +591,8 @@ def run_workload(args, torch, F, W, w):
         aux["warm_cache_resident_us_per_call"] = round(ms_warm * 1e3, 3)
         aux["warm_cache_resident_kernel_us"] = round(statistics.mean(kern_warm) * 1e3, 3)
 
+    if probes:
+        aux["machine"] = probes
     traffic = traffic_for(w.name, plan["variant"])
     rec = {
         "metric": METRIC,
@@ -443,7 +612,8 @@ def run_workload(args, torch, F, W, w):
                    "n_kv_head": w.n_kv_head, "n_tok": w.n_tok, "n_kv": w.n_kv, "n_valid": w.n_valid, "hd": w.hd,
                    "q_dtype": w.q_dtype, "variant": args.variant,
                    "round_f16": bool(args.round_f16)},
-        "roofline": roofline(w, kern_ms, achieved, traffic),
+        "roofline": roofline(w, kern_ms, achieved, traffic, ms_call,
+                             call_traffic_for(w.name, plan["variant"])),
         "aux": aux,
     }
     if not args.no_cpu_baseline:
@@ -599,6 +769,7 @@ def main(argv=None):
     F.binding.load()
     names = ([w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS] + [COPY_WORKLOAD, QKV_WORKLOAD]
              if args.workload == "all" else [args.workload])
+    probes = None if args.no_probes else machine_probes(torch)
     for name in names:
         if name == COPY_WORKLOAD:
             print(json.dumps(run_copy_workload(args, torch, F)), flush=True)
@@ -609,7 +780,7 @@ def main(argv=None):
         if name not in W.BY_NAME:
             print(f"unknown workload {name}; choose from {list(W.BY_NAME)}", file=sys.stderr)
             return 1
-        rec = run_workload(args, torch, F, W, W.BY_NAME[name])
+        rec = run_workload(args, torch, F, W, W.BY_NAME[name], probes)
         print(json.dumps(rec), flush=True)
     return 0
 
