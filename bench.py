@@ -363,8 +363,11 @@ def machine_probes(torch):
     - HBM read rates: one workgroup (one compute unit) streaming 1 MiB it has
       not touched before (caches scrubbed by a 512 MiB read elsewhere) with
       32 KiB or 128 KiB of loads in flight, and 256 workgroups streaming 1 MiB
-      each (the whole chip);
-    - merging key-split partials: 256 workgroups in groups of 4 or 8, each
+      each (the whole chip); and the chip's rate for reads served by L2 (the
+      workgroups of one XCD reading the same 512 KiB) against distinct data;
+    - the LDS read rate of one workgroup with one or two waves per SIMD, for
+      the 16-byte reads of K and the transposing reads of V;
+    - merging key-split partials: 256 workgroups in groups of 2, 4 or 8, each
       reading 64 KiB and writing a 48 KiB partial; the merge as a second
       launch against one launch whose last-arriving workgroup merges its group
       (agent-scope acquire/release fences, or device-coherent sc1 accesses),
@@ -377,7 +380,9 @@ def machine_probes(torch):
     lib.frp_empty.argtypes = [i32, i32, vp]
     lib.frp_read.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     lib.frp_merge.argtypes = [i32, vp, vp, vp, vp, i32, i32, vp]
-    for f in (lib.frp_empty, lib.frp_read, lib.frp_merge):
+    lib.frp_lds.argtypes = [i32, i32, i32, vp, vp, vp]
+    lib.frp_read_shared.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    for f in (lib.frp_empty, lib.frp_read, lib.frp_merge, lib.frp_lds, lib.frp_read_shared):
         f.restype = i32
     grid, pf, wb = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     lib.frp_merge_sizes(ctypes.byref(grid), ctypes.byref(pf), ctypes.byref(wb))
@@ -444,7 +449,31 @@ def machine_probes(torch):
                                                               * 10.0), 1)
     res["read_chip_per_workgroup_GBps"] = round(float(np.median(per / ((t[:, 1] - t[:, 0])
                                                                        * 10.0))), 1)
-    del times, sink
+    # the same reads served by L2: 256 workgroups of 512 lanes reading 512 KiB twice,
+    # either 8 regions (each shared by the 32 workgroups of one XCD) or all distinct
+    t3 = torch.zeros(3 * 256, dtype=torch.int64, device="cuda")
+    for n_region, label in ((8, "shared_by_xcd"), (256, "distinct")):
+        scrub()
+        ok(lib.frp_read_shared(base + 512 * mib, 512 << 10, 256, n_region, t3.data_ptr(),
+                               sink.data_ptr(), stream), "read_shared")
+        torch.cuda.synchronize()
+        t = t3.cpu().numpy().reshape(256, 3)
+        res[f"read_chip_second_pass_{label}_GBps"] = round(
+            256 * (512 << 10) / ((t[:, 2].max() - t[:, 1].min()) * 10.0), 1)
+    del times, sink, t3
+
+    # LDS read rate of one workgroup (bytes per ns; at 2.4 GHz, / 2.4 = bytes per clock)
+    t2 = torch.zeros(2, dtype=torch.int64, device="cuda")
+    s2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for kind, kname, per_lane in ((0, "b128", 16), (1, "tr_b16_b64", 8)):
+        for lanes in (256, 512):
+            iters = 2000
+            ok(lib.frp_lds(kind, lanes, iters, t2.data_ptr(), s2.data_ptr(), stream), "lds")
+            torch.cuda.synchronize()
+            tt = t2.cpu().numpy()
+            res[f"lds_{kname}_bytes_per_ns_{lanes // 256}_waves_per_simd"] = round(
+                iters * 16 * per_lane * lanes / ((tt[1] - tt[0]) * 10.0), 1)
+    del t2, s2
 
     # merging key-split partials: two launches against one
     part = torch.zeros(grid * pf, dtype=torch.float32, device="cuda")
@@ -455,7 +484,7 @@ def machine_probes(torch):
     merge = {}
     names = {0: "two_launches", 1: "one_launch_fenced", 2: "one_launch_sc1",
              3: "one_launch_sliced", 4: "one_launch_waiting_combine"}
-    for n_split in (4, 8):
+    for n_split in (2, 4, 8):
         for mode in (0, 1, 2, 3, 4):
             calls = 40
             for it in range(4):            # warm-up

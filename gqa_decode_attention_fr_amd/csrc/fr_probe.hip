@@ -16,6 +16,7 @@
 namespace {
 
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint64_t clock100() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -48,6 +49,83 @@ __global__ __launch_bounds__(256) void read_kernel(const float4v *src, int64_t n
     times[2 * blockIdx.x + 1] = t1;
   }
   if (acc == -1.f) sink[blockIdx.x] = acc;   // keeps the loads (the data is never -1 in sum)
+}
+
+// Workgroup b reads n16 granules at src + (b % n_region)*n16 twice (the
+// workgroups of one region share it, in L2 where they run on one XCD; workgroup
+// b runs on XCD b % 8); times[3b .. 3b+2] = start, end of pass 1, end of pass 2.
+__global__ __launch_bounds__(512) void shared_read_kernel(const float4v *src, int64_t n16,
+                                                          int n_region, uint64_t *times,
+                                                          float *sink) {
+  const float4v *p = src + (int64_t)(blockIdx.x % n_region) * n16;
+  float acc = 0.f;
+  uint64_t t[3];
+  __syncthreads();
+  t[0] = clock100();
+  for (int ps = 0; ps < 2; ++ps) {
+    for (int64_t i = threadIdx.x; i < n16; i += 512 * 8) {
+      float4v v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = i + u * 512;
+        v[u] = j < n16 ? p[j] : float4v{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+    }
+    __syncthreads();
+    t[ps + 1] = clock100();
+  }
+  if (threadIdx.x == 0) {
+    times[3 * blockIdx.x] = t[0];
+    times[3 * blockIdx.x + 1] = t[1];
+    times[3 * blockIdx.x + 2] = t[2];
+  }
+  if (acc == -1.f) sink[blockIdx.x] = acc;
+}
+
+// LDS read rate of one workgroup of NT lanes: each lane reads 16 bytes per
+// ds_read_b128 (KIND 0) or 8 per ds_read_b64_tr_b16 (KIND 1), 16 reads issued
+// back to back per trip (the compiler waits for them as their results are
+// used), iters trips; times[0], times[1] bracket the reads.
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+template <int KIND, int NT>
+__global__ __launch_bounds__(NT) void lds_read_kernel(uint64_t *times, uint32_t *sink,
+                                                      int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[16384];   // 64 KiB
+  for (int i = threadIdx.x; i < 16384; i += NT) lds[i] = (uint32_t)i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int base = (wave * 256 + lane * 4) & 1023;   // 16-byte slots, uint32 index
+  uint32_t acc = 0;
+  __syncthreads();
+  const uint64_t t0 = clock100();
+  for (int it = 0; it < iters; ++it) {
+    if (KIND == 0) {
+      uint4v r[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        r[u] = *(const uint4v *)&lds[(base + u * 1024 + it) & 16380];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc ^= r[u].x ^ r[u].w;
+    } else {
+      typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4;
+      fp16x4 r[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        r[u] = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (__attribute__((address_space(3))) fp16x4 *)&lds[(base + u * 1024 + 2 * it) & 16382]);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc ^= __builtin_bit_cast(uint2v, r[u]).x;
+    }
+  }
+  __syncthreads();
+  const uint64_t t1 = clock100();
+  if (threadIdx.x == 0) {
+    times[0] = t0;
+    times[1] = t1;
+  }
+  if (acc == 0xdeadbeefu) sink[0] = acc;
 }
 
 // ---- merge probe.  kMergeGrid workgroups of 256 lanes form groups of n_split
@@ -292,6 +370,36 @@ int frp_read(const void *src, int64_t bytes_per_wg, int n_wg, int unroll, uint64
                        (const float4v *)src, n16, times, sink);
   else
     return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// n_wg workgroups of 512 lanes, workgroup b reading (twice) the bytes_per_wg
+// bytes at src + (b % n_region)*bytes_per_wg; src must hold
+// n_region*bytes_per_wg bytes, times 3*n_wg uint64, sink n_wg floats.
+int frp_read_shared(const void *src, int64_t bytes_per_wg, int n_wg, int n_region,
+                    uint64_t *times, float *sink, void *stream) {
+  if (!src || !times || !sink || n_wg < 1 || n_wg > 65536 || n_region < 1 ||
+      bytes_per_wg < 16 || bytes_per_wg % 16 || ((uintptr_t)src % 16))
+    return -1;
+  hipLaunchKernelGGL(shared_read_kernel, dim3(n_wg), dim3(512), 0, (hipStream_t)stream,
+                     (const float4v *)src, bytes_per_wg / 16, n_region, times, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// One workgroup reading LDS: kind 0 = ds_read_b128, 1 = ds_read_b64_tr_b16;
+// 256 or 512 lanes (one or two waves per SIMD); times 2 uint64, sink 1 uint32.
+int frp_lds(int kind, int lanes, int iters, uint64_t *times, uint32_t *sink, void *stream) {
+  if (!times || !sink || iters < 1 || (kind != 0 && kind != 1) || (lanes != 256 && lanes != 512))
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == 0 && lanes == 256)
+    hipLaunchKernelGGL((lds_read_kernel<0, 256>), dim3(1), dim3(256), 0, s, times, sink, iters);
+  else if (kind == 0)
+    hipLaunchKernelGGL((lds_read_kernel<0, 512>), dim3(1), dim3(512), 0, s, times, sink, iters);
+  else if (lanes == 256)
+    hipLaunchKernelGGL((lds_read_kernel<1, 256>), dim3(1), dim3(256), 0, s, times, sink, iters);
+  else
+    hipLaunchKernelGGL((lds_read_kernel<1, 512>), dim3(1), dim3(512), 0, s, times, sink, iters);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
