@@ -46,6 +46,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <utility>
 
 #include "fr_device.h"
@@ -59,6 +60,26 @@ namespace {
 // 16 token rows (kMaskReg) or, in the 8-wave shape, 64 (kMaskReg64, which
 // needs four times the staging registers).
 enum MaskMode { kMaskNone = 0, kMaskDma = 1, kMaskReg = 2, kMaskReg64 = 3 };
+
+// First work item of XCD x when W items are dealt to the 8 XCDs in
+// contiguous, balanced ranges (XCDs below W % 8 take one more).
+__host__ __device__ __forceinline__ int xcd_item_start(int x, int W) {
+  return x * (W >> 3) + min(x, W & 7);
+}
+
+// The XCD holding most of the items [k0, k0 + n) (the lowest on a tie).
+int xcd_majority(int k0, int n, int W) {
+  int best = 0, best_n = -1;
+  for (int x = 0; x < 8; ++x) {
+    const int lo = std::max(k0, xcd_item_start(x, W));
+    const int hi = std::min(k0 + n, xcd_item_start(x + 1, W));
+    if (hi - lo > best_n) {
+      best_n = hi - lo;
+      best = x;
+    }
+  }
+  return best;
+}
 
 struct SplitArgs {
   const void *q;
@@ -274,19 +295,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   const int g = lane >> 4;
 
   // Workgroup -> (unit, key split, row block).  Workgroup b runs on XCD
-  // b % 8, and each XCD has its own L2: the row blocks of one (unit, split)
-  // pair read the same K/V chunk, so they take workgroups 8 apart (the
-  // same XCD, dispatched close together).  Pairs x = unit*n_split + split go
-  // in groups of 8 (fewer in the last group): group gr holds its pairs' row
-  // block 0, then row block 1, ...
-  const int n_pair = gridDim.x / a.n_rowblk;
-  const int gr = blockIdx.x / (8 * a.n_rowblk);
-  const int in_gr = blockIdx.x - gr * 8 * a.n_rowblk;
-  const int gcnt = min(8, n_pair - 8 * gr);
+  // b % 8, and each XCD has its own L2.  Work items k = pair*n_rowblk + rowblk
+  // (pair = unit*n_split + split) are dealt to the XCDs in contiguous,
+  // balanced ranges (xcd_item_start): the row blocks of a pair, which read the
+  // same K/V chunk, and the key splits of a unit, which read the same queries,
+  // share an L2 (a unit spans at most two XCDs when it has fewer items than
+  // an XCD), and where the combine kernel merges a unit on the XCD that wrote
+  // most of its partials, it finds them in that L2.
+  const int xcd = blockIdx.x & 7;
+  const int item = xcd_item_start(xcd, gridDim.x) + (blockIdx.x >> 3);
   // (integer division runs on the vector unit; the results are uniform and
   // are moved back to scalar registers, so addresses built from them are too)
-  const int rowblk = __builtin_amdgcn_readfirstlane(in_gr / gcnt);
-  const int pair = 8 * gr + in_gr - rowblk * gcnt;
+  const int rowblk = __builtin_amdgcn_readfirstlane(item % a.n_rowblk);
+  const int pair = __builtin_amdgcn_readfirstlane(item / a.n_rowblk);
   const int split = __builtin_amdgcn_readfirstlane(pair % a.n_split);
   // the unit (instance, KV head) of this workgroup; its partials are indexed
   // by the unit, its inputs and output by the instance and the KV head
@@ -463,10 +484,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   for (int i = 0; i < TPW; ++i) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      // Lanes of rows past the tile's valid rows hold row 0's (finite) values:
+      // their scores and outputs are computed and never stored.  Only the
+      // columns past HDD (hd 80 in the hd-128 layout) must be zero, as they
+      // meet K granules in the scores.
       const float4v zero = {0.f, 0.f, 0.f, 0.f};
       const bool on = q_on[i] && ks * 32 + g * 8 < HDD;
-      const float4v x0 = on ? qraw[i][ks][0] : zero;
-      const float4v x1 = on ? qraw[i][ks][1] : zero;
+      const float4v x0 = (HDD < HD && !on) ? zero : qraw[i][ks][0];
+      const float4v x1 = (HDD < HD && !on) ? zero : qraw[i][ks][1];
       if (QMODE == kQF16) {
         qh[i][ks] = __builtin_bit_cast(half8, x0);
         ql[i][ks] = half8{};
@@ -480,7 +505,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
           qh[i][ks][e] = h.x;
           qh[i][ks][e + 1] = h.y;
           if (QMODE == kQHiLo) {
-            const float2v r = {fmaf((float)h.x, -1.f, x[e]), fmaf((float)h.y, -1.f, x[e + 1])};
+            // x - hi in one mixed-precision fma per element, hi read as f16
+            // from its half of the packed pair (exact: one rounding of an
+            // exactly representable difference)
+            const uint32_t hp = __builtin_bit_cast(uint32_t, h);
+            float2v r;
+            asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]"
+                : "=v"(r.x) : "v"(hp), "v"(x[e]));
+            asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                : "=v"(r.y) : "v"(hp), "v"(x[e + 1]));
             const half2v lo = __builtin_convertvector(r, half2v);
             ql[i][ks][e] = lo.x;
             ql[i][ks][e + 1] = lo.y;
@@ -910,6 +943,11 @@ struct CombineArgs {
   int64_t out_stride;
   int M, n_split, n_inst;   // n_inst counts units (instance, KV head)
   int n_kvh, grp, n_head;
+  // XCD-local merging (the kernel's LOCAL instance): the workgroups on XCD x
+  // (workgroup b runs on XCD b % 8) merge units [ub[x], ub[x+1]), wpu
+  // workgroups per unit; else the rows of all units are dealt out in order.
+  int xcd_local, wpu;
+  int ub[9];
 };
 
 // NT threads = RW rows x G split groups x (HD/4) columns of 4 consecutive d,
@@ -922,7 +960,7 @@ struct CombineArgs {
 // A split with no visible key has m_s = -inf and weight 0; a row with no
 // visible key at all is written as zeros.  The merge order is fixed, so the
 // result does not depend on timing.
-template <int HD, int G, int NT>
+template <int HD, int G, int NT, bool LOCAL>
 __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   constexpr int C = HD / 4;          // float4 columns per row
   constexpr int RW = NT / (C * G);   // rows per workgroup
@@ -934,10 +972,21 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   const int c = threadIdx.x % C;
   const int g = (threadIdx.x / C) % G;
   const int rw = threadIdx.x / (C * G);
-  const int row = blockIdx.x * RW + rw;          // over units * M
-  const bool on = row < a.n_inst * a.M;
-  const int r = on ? row % a.M : 0;
-  const int inst = on ? row / a.M : 0;
+  bool on;
+  int r, inst;
+  if (LOCAL) {
+    const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+    const int unit = a.ub[xcd] + jx / a.wpu;
+    const int row = (jx % a.wpu) * RW + rw;        // row of the unit
+    on = unit < a.ub[xcd + 1] && row < a.M;
+    r = on ? row : 0;
+    inst = on ? unit : 0;
+  } else {
+    const int row = blockIdx.x * RW + rw;          // over units * M
+    on = row < a.n_inst * a.M;
+    r = on ? row % a.M : 0;
+    inst = on ? row / a.M : 0;
+  }
   const int64_t base = (int64_t)inst * a.n_split;
 
   float m = -INFINITY, l = 0.f;
@@ -953,8 +1002,15 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
       if (sp < a.n_split) {
         const int64_t prow = (base + sp) * a.M + r;
         ml[j] = a.part_ml[prow];
-        // streaming loads: each partial is read once
-        po[j] = __builtin_nontemporal_load((const float4v *)(a.part_o + prow * HD + 4 * c));
+        // each partial is read once: merged on the XCD that wrote it, an
+        // ordinary load finds it in that L2; otherwise a streaming load
+        // (measured: pi0.5 step -0.5 us with ordinary loads XCD-locally;
+        // long context +2.2 us and the prefill +2.9 with them elsewhere)
+        const float4v *src = (const float4v *)(a.part_o + prow * HD + 4 * c);
+        if constexpr (LOCAL)
+          po[j] = *src;
+        else
+          po[j] = __builtin_nontemporal_load(src);
       }
     }
     float mc = m;
@@ -1008,31 +1064,49 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
 // per call, f16-Q -0.38); else 256 (larger grids, such as a prefill's, were
 // slower with 128).
 template <int HD>
-hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
+hipError_t launch_combine(CombineArgs c, hipStream_t stream) {
   constexpr int C = HD / 4;
   const int rows = c.n_inst * c.M;
+  // workgroups for RW rows each: one per RW rows in order, or, XCD-local,
+  // 8 x (most units on one XCD) x (workgroups per unit), some of them idle
+  auto grid = [&](int RW) {
+    if (!c.xcd_local) return (rows + RW - 1) / RW;
+    c.wpu = (c.M + RW - 1) / RW;
+    int most = 0;
+    for (int x = 0; x < 8; ++x) most = std::max(most, c.ub[x + 1] - c.ub[x]);
+    return 8 * most * c.wpu;
+  };
   auto go = [&](auto GI) {
     constexpr int GN = decltype(GI)::value;   // split groups wanted
     if constexpr ((C & (C - 1)) != 0) {
       // hd 80: 20 columns; workgroups of 160 threads (320 for 16 groups)
       constexpr int NT = GN * C <= 160 ? 160 : 320;
       constexpr int RW = NT / (C * GN);
-      hipLaunchKernelGGL((combine_kernel<HD, GN, NT>), dim3((rows + RW - 1) / RW), dim3(NT), 0,
-                         stream, c);
+      const int wgs = grid(RW);
+      if (c.xcd_local)
+        hipLaunchKernelGGL((combine_kernel<HD, GN, NT, true>), dim3(wgs), dim3(NT), 0, stream, c);
+      else
+        hipLaunchKernelGGL((combine_kernel<HD, GN, NT, false>), dim3(wgs), dim3(NT), 0, stream, c);
       return hipGetLastError();
     } else {
       if constexpr (GN * C <= 128) {
         constexpr int RW = 128 / (C * GN);
-        const int wgs = (rows + RW - 1) / RW;
-        if (wgs < 1024) {
-          hipLaunchKernelGGL((combine_kernel<HD, GN, 128>), dim3(wgs), dim3(128), 0, stream, c);
+        if ((rows + RW - 1) / RW < 1024) {
+          const int wgs = grid(RW);
+          if (c.xcd_local)
+            hipLaunchKernelGGL((combine_kernel<HD, GN, 128, true>), dim3(wgs), dim3(128), 0, stream, c);
+          else
+            hipLaunchKernelGGL((combine_kernel<HD, GN, 128, false>), dim3(wgs), dim3(128), 0, stream, c);
           return hipGetLastError();
         }
       }
       constexpr int G = GN < 256 / C ? GN : 256 / C;
       constexpr int RW = 256 / (C * G);
-      hipLaunchKernelGGL((combine_kernel<HD, G, 256>), dim3((rows + RW - 1) / RW), dim3(256), 0,
-                         stream, c);
+      const int wgs = grid(RW);
+      if (c.xcd_local)
+        hipLaunchKernelGGL((combine_kernel<HD, G, 256, true>), dim3(wgs), dim3(256), 0, stream, c);
+      else
+        hipLaunchKernelGGL((combine_kernel<HD, G, 256, false>), dim3(wgs), dim3(256), 0, stream, c);
       return hipGetLastError();
     }
   };
@@ -1146,6 +1220,21 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, void *workspace, hip
   c.n_kvh = p.n_kvh;
   c.grp = p.grp();
   c.n_head = p.n_head;
+  // XCD-local merging where each unit's work items fit in one XCD's share of
+  // the split kernel's grid (so each unit's partials lie on one or two XCDs);
+  // a unit is merged on the XCD holding most of its items
+  const int ipu = plan.n_split * plan.n_rowblk;
+  c.xcd_local = ipu <= plan.grid / 8 ? 1 : 0;
+  c.wpu = 0;
+  c.ub[0] = 0;
+  if (c.xcd_local) {
+    int x_prev = 0, u = 0;
+    for (; u < p.units(); ++u) {
+      const int x = xcd_majority(u * ipu, ipu, plan.grid);
+      for (; x_prev < x; ++x_prev) c.ub[x_prev + 1] = u;
+    }
+    for (; x_prev < 8; ++x_prev) c.ub[x_prev + 1] = u;
+  }
   switch (p.hd) {
     case 64: return launch_combine<64>(c, stream);
     case 80: return launch_combine<80>(c, stream);
