@@ -48,29 +48,43 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
     // more query tokens than a 4-wave workgroup stages mask rows for
     if (!unmasked && n_tok > max_tokens(4)) p.waves = 8;
   }
-  // Row blocks of at most waves*tiles tiles, balanced: with 5 tiles and room
-  // for 4, blocks of 3 and 2 rather than 4 and 1 (the largest block sets the
-  // per-workgroup query loads and partial stores).
-  const int tiles_cap = p.waves * p.tiles;
-  p.n_rowblk = (int)cdiv(tiles_total, tiles_cap);
-  p.tpr = p.variant == kFused ? (int)cdiv(tiles_total, p.n_rowblk) : tiles_cap;
   const int key_blocks = (int)cdiv(n_kv, kKeyBlock);
-  // Key splits: as many as keep the grid within one workgroup per compute
-  // unit.  Where that leaves a single key block per split, two blocks per
-  // split are taken instead if the grid still covers half the machine: the
-  // partials (and their combine) then halve, and block 1 loads while block 0
-  // is computed.
-  const int64_t wg_per_split = (int64_t)n_inst * p.n_rowblk;
-  int want = (int)std::max<int64_t>(1, kTargetWorkgroups / wg_per_split);
-  if (cdiv(key_blocks, want) < 2 && wg_per_split * cdiv(key_blocks, 2) >= kTargetWorkgroups / 2)
-    want = (int)cdiv(key_blocks, 2);
   const int forced = env_int("FR_FORCE_SPLITS", 0);
-  if (forced > 0) want = forced;
-  want = std::min(std::max(want, 1), key_blocks);
-  const int blocks_per_split = (int)cdiv(key_blocks, want);
-  p.chunk = blocks_per_split * kKeyBlock;
-  p.n_split = (int)cdiv(key_blocks, blocks_per_split);
-  p.grid = n_inst * p.n_rowblk * p.n_split;
+  // Row blocks of at most tiles_cap tiles, balanced: with 5 tiles and room
+  // for 4, blocks of 3 and 2 rather than 4 and 1 (the largest block sets the
+  // per-workgroup query loads and partial stores).  Key splits: as many as
+  // keep the grid within one workgroup per compute unit.  Where that leaves a
+  // single key block per split, two blocks per split are taken instead if the
+  // grid still covers half the machine: the partials (and their combine) then
+  // halve, and block 1 loads while block 0 is computed.
+  auto decompose = [&](int tiles_cap) {
+    p.n_rowblk = (int)cdiv(tiles_total, tiles_cap);
+    p.tpr = p.variant == kFused ? (int)cdiv(tiles_total, p.n_rowblk) : tiles_cap;
+    const int64_t wg_per_split = (int64_t)n_inst * p.n_rowblk;
+    int want = (int)std::max<int64_t>(1, kTargetWorkgroups / wg_per_split);
+    if (cdiv(key_blocks, want) < 2 && wg_per_split * cdiv(key_blocks, 2) >= kTargetWorkgroups / 2)
+      want = (int)cdiv(key_blocks, 2);
+    if (forced > 0) want = forced;
+    want = std::min(std::max(want, 1), key_blocks);
+    const int blocks_per_split = (int)cdiv(key_blocks, want);
+    p.chunk = blocks_per_split * kKeyBlock;
+    p.n_split = (int)cdiv(key_blocks, blocks_per_split);
+    p.grid = n_inst * p.n_rowblk * p.n_split;
+  };
+  decompose(p.waves * p.tiles);
+  // Where the key blocks cap the splits and row blocks of four tiles leave the
+  // grid below three quarters of the machine (the f16-Q workload: 128
+  // workgroups; the causal tail: 64), row blocks of at most two tiles double
+  // the grid and halve each workgroup's query loads and partial stores (its
+  // other waves only stage K/V): f16-Q 11.0 -> 10.4 us per call, causal tail
+  // 12.4 -> 11.5.  Row blocks of one tile, or this rule on the pi0.5 step's
+  // 216 workgroups, were slower.
+  if (p.variant == kFused && p.waves == 4 && p.tiles == 1 && p.grid < 3 * kTargetWorkgroups / 4 &&
+      env_int("FR_FORCE_WAVES", 0) == 0) {
+    const Plan four = p;
+    decompose(2);
+    if (p.grid > kTargetWorkgroups) p = four;   // only while the grid still fits the machine
+  }
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t rows = (size_t)n_inst * p.n_split * M;
   if (p.variant == kFused) {
