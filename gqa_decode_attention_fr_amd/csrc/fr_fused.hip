@@ -21,10 +21,13 @@
 //   b+1 is in flight while block b is computed.  Waits are explicit vmcnt
 //   counts ahead of a plain s_barrier.
 //   each wave, for its tile:
-//     S^T = K . Q^T       v_mfma_f32_16x16x32_f16, fp32 accumulation; an f32 Q
-//                         enters as hi + lo f16 halves (two MFMAs)
-//     online softmax      scale*log2(e) folded in, exp2, block max shared by
-//                         the four lane groups of a row through two shuffles
+//     S^T = K . Q^T + C   v_mfma_f32_16x16x32_f16, fp32 accumulation; an f32 Q
+//                         enters as hi + lo f16 halves (two MFMAs) carrying
+//                         scale*log2(e); the accumulator starts from the mask
+//                         and minus the row's reference max, so the scores
+//                         leave the matrix core as base-2 logits
+//     online softmax      a lazy reference max (moved rarely, by a threshold
+//                         test and two shuffles), exp2, f16 probabilities
 //     O^T += V^T . P^T    V^T operand read with ds_read_b64_tr_b16 straight
 //                         from V's natural [key][d] layout; P is unnormalised f16
 //   n_split == 1: out = O / l;  n_split > 1: (O, m, l) partials merged by the
@@ -172,9 +175,10 @@ __device__ __forceinline__ half4 lds_tr16(const _Float16 *p) {
   return __builtin_bit_cast(half4, v);
 }
 
-// Lazy softmax reference: the running max moves only when a block's max is
-// more than 8*ln(2) above it, so unnormalised probabilities stay <= 2^8.
-constexpr float kLazy = 5.545177444479562f;
+// Lazy softmax reference: the running max moves only when a block's logits
+// exceed it by more than 8 (base-2 units), so unnormalised probabilities stay
+// <= 2^8.
+constexpr float kLazy2 = 8.f;
 
 // Reductions over the four lanes l, l^16, l^32, l^48 (the four lane groups
 // that share one query row) with gfx950's VALU row swaps, no LDS traffic:
@@ -497,8 +501,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
         ql[i][ks] = half8{};
       } else {
         // pairs: hi = f16(x) (round to nearest even, packed), lo = f16(x - hi)
-        // with the difference taken exactly in one mixed-precision fma
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        // with the difference taken exactly in one mixed-precision fma.  The
+        // split queries carry scale*log2(e), so the scores come out of the
+        // matrix core as base-2 logits; a single rounding (kQRound) stays
+        // unscaled, so that it equals the pre-rounded f16 input bit for bit.
+        const float qs = QMODE == kQHiLo ? a.scale * kLog2e : 1.f;
+        const float x[8] = {x0.x * qs, x0.y * qs, x0.z * qs, x0.w * qs,
+                            x1.x * qs, x1.y * qs, x1.z * qs, x1.w * qs};
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const half2v h = __builtin_convertvector(float2v{x[e], x[e + 1]}, half2v);
@@ -526,31 +535,43 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     }
   }
 
-  // m_run: reference max in natural-log units; lacc: running row sums (all four
-  // elements equal); o: unnormalised output tiles
-  float m_run[TPW], m_thr[TPW], nbv[TPW], alpha[TPW];
+  // Online-softmax state of each tile row, in "score units" u: the scores the
+  // matrix core produces are base-2 logits times 1/su, where su = 1 for split
+  // queries (they carry scale*log2(e)) and su = scale*log2(e) for f16 queries.
+  //   ref: the reference max (base-2 logit units), 0 until the row has seen a
+  //        key (ref_set false), then moved up only by more than kLazy2
+  //   cb:  -ref/su, the reference as it enters the score accumulator; cq is
+  //        cb in all four elements (the accumulator start of unmasked calls)
+  //   thr: a half's logits above it move the reference: kLazy2/su once set,
+  //        -inf before (the row's first visible key sets it)
+  //   adj: what half 0 moved the reference by, for half 1 of the same block
+  //        (its accumulators started from the old reference)
+  // lacc: running row sums (all four elements equal); o: unnormalised output
+  constexpr bool kScaledQ = QMODE == kQHiLo;
+  const float su = kScaledQ ? 1.f : a.scale * kLog2e;
+  const float inv_su = kScaledQ ? 1.f : 1.f / su;
+  const float mmul = kLog2e * inv_su;    // mask (natural-log units) into score units
+  float ref[TPW], cb[TPW], thr[TPW], adj[TPW], alpha[TPW];
+  bool ref_set[TPW];
+  float4v cq[TPW];
   float4v lacc[TPW];
   float4v o[TPW][DT];
   const half8 kOnes = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
                        (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
-    m_run[i] = -INFINITY;
-    m_thr[i] = -INFINITY;
-    nbv[i] = 0.f;
+    ref[i] = 0.f;
+    cb[i] = 0.f;
+    thr[i] = -INFINITY;
+    adj[i] = 0.f;
     alpha[i] = 1.f;
+    ref_set[i] = false;
+    cq[i] = float4v{0.f, 0.f, 0.f, 0.f};
     lacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[i][dt] = float4v{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- per-lane LDS byte offsets.  With the swizzles above, the XOR term of
-  // a K read depends on the lane and on ks mod 4 only, and that of a V read on
-  // the lane and dt mod 8 only; everything else is a compile-time immediate.
-  //   K row of score tile kt, lane q = l16:  32*(kt/2) + 4*(kt%2) + [8*(q/4) + q%4]
-  //   K slot of step ks: (4*ks + g) ^ swz_k(row) = 16*(ks/4) + ((4*(ks%4) + g) ^ (q % GPR))
-  //   V rows of a transposing read: 32*hh + 4*e + [8*g + q/4]
-  //   V slot of tile dt: 16*(dt/8) + ((2*(dt%8) + (q%4)/2) ^ swz_v(row)), swz_v lane-constant
   constexpr int NKO = KS < 4 ? KS : 4;
   constexpr int NVO = DT < 8 ? DT : 8;
 
@@ -598,77 +619,78 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
   // ---- one 64-key block, as a software pipeline over its two 32-key halves.
   // The MFMA work of one half runs while the softmax (VALU) of the other half
   // is issued between its steps, so the two units overlap inside a wave:
-  //   A: S^T(h0) = K(h0).Q^T
-  //   B: S^T(h1) = K(h1).Q^T       with softmax(h0) steps in between
-  //   C: O^T += V^T(h0).P^T(h0)    with softmax(h1) steps in between
+  //   A: S^T(h0) = K(h0).Q^T + C(h0)
+  //   B: S^T(h1) = K(h1).Q^T + C(h1)   with softmax(h0) steps in between
+  //   C: O^T += V^T(h0).P^T(h0)        with softmax(h1) steps in between
   //   D: O^T += V^T(h1).P^T(h1)
-  // Each half updates the online-softmax state on its own; a rescale of the
-  // output (rare: the reference max only moves by more than kLazy) is applied
-  // between stages, before the PV of the half that moved it.
-  float yv[TPW][8];   // logits, then probabilities, of the half in flight
-  float bmv[TPW];     // block max of the half in flight
+  // The score accumulators start from C = mask*log2(e)/su - ref/su (keys past
+  // the split's end: -inf), so the matrix core delivers each logit already
+  // masked and relative to the reference: the softmax of a half is a
+  // threshold test, exp2 and a conversion (the f16-query modes multiply by su
+  // first).  Each half updates the state on its own; a rescale of the output
+  // (rare: the reference moves only by more than kLazy2) is applied between
+  // stages, before the PV of the half that moved it.
+  float yv[TPW][8];   // probabilities of the half in flight
+  float bmv[TPW];     // largest logit of this lane in the half in flight
   bool moved = false;
+  bool pend = false;  // half 0 moved a reference after half 1's accumulators started
   half8 pb[TPW][2];   // P^T of the two halves, the PV B operand
 
   // Step ST (0..7) of the softmax of half HH for every tile of the wave.
-  auto sm_step = [&](auto STEP, auto HH, bool ragged, const half8 (&mh)[TPW][2],
-                     const float4v (&sc)[TPW][4], int kb0) __attribute__((always_inline)) {
+  auto sm_step = [&](auto STEP, auto HH, float4v (&sc)[TPW][4]) __attribute__((always_inline)) {
     constexpr int st = decltype(STEP)::value;
     constexpr int hh = decltype(HH)::value;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      if constexpr (st <= 1) {
-        // scale + mask in natural-log units; keys of tile kt = 2hh+st are
-        // 32hh + 8g + 4st + e for e < 4
+      if constexpr (st == 0) {
+        if (hh == 1 && pend) {   // (uniform, rare) half 0 moved the reference
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float m = MASKMODE != kMaskNone ? (float)mh[i][hh][4 * st + e] : 0.f;
-          yv[i][4 * st + e] = fmaf(sc[i][2 * hh + st][e], a.scale, m);
-          pin(yv[i][4 * st + e]);
+          for (int j = 0; j < 2; ++j) sc[i][2 + j] -= adj[i];
         }
-        if (ragged) {   // uniform: only the block holding the split's end
-          const int k0 = kb0 + 32 * hh + 8 * g + 4 * st;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (k0 + e >= key_end) yv[i][4 * st + e] = -INFINITY;
-        }
+      } else if constexpr (st == 1) {
+        // keys of tile kt = 2hh+j are 32hh + 8g + 4j + e for e < 4
+        const float4v &s0 = sc[i][2 * hh], &s1 = sc[i][2 * hh + 1];
+        bmv[i] = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                       fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        pin(bmv[i]);
       } else if constexpr (st == 2) {
-        float bm = fmaxf(fmaxf(yv[i][0], yv[i][1]), yv[i][2]);
-        bm = fmaxf(fmaxf(bm, yv[i][3]), yv[i][4]);
-        bmv[i] = fmaxf(fmaxf(bm, yv[i][5]), fmaxf(yv[i][6], yv[i][7]));
-        pin(bmv[i]);
-      } else if constexpr (st == 3) {
-        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmv[i]), __float_as_uint(bmv[i]),
-                                                  false, false);
-        bmv[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        pin(bmv[i]);
-      } else if constexpr (st == 4) {
-        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmv[i]), __float_as_uint(bmv[i]),
-                                                  false, false);
-        const float bm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        const float m_old = m_run[i];
-        // moves when bm exceeds the reference by more than kLazy; also taken
-        // when m_old = -inf and bm is finite (alpha = 2^-inf = 0 then).  The
-        // common case costs one compare and a uniform branch.
-        const bool mv = bm > m_thr[i];   // m_thr = m_run + kLazy
-        if (__any(mv)) {                   // rare: the reference max moves
-          alpha[i] = mv ? fast_exp2((m_old - bm) * kLog2e) : 1.f;
-          m_run[i] = mv ? bm : m_old;
-          m_thr[i] = m_run[i] + kLazy;
-          nbv[i] = (m_run[i] == -INFINITY) ? 0.f : -m_run[i] * kLog2e;
+        // The common case costs one compare and a uniform branch.  A move
+        // takes the row's largest logit over its four lane groups as the new
+        // reference (relative: d); before the row has seen a key its logits
+        // are relative to 0 and o, lacc are still zero.
+        const bool mv = bmv[i] > thr[i];
+        if (__any(mv)) {
+          const float rm = group_max(bmv[i]);
+          const bool mvr = rm > thr[i];
+          const float d = mvr ? rm : 0.f;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) sc[i][2 * hh + j] -= d;
+          alpha[i] = (mvr && ref_set[i]) ? fast_exp2(-d * su) : 1.f;
+          ref[i] += d * su;
+          ref_set[i] = ref_set[i] || mvr;
+          thr[i] = ref_set[i] ? kLazy2 * inv_su : -INFINITY;
+          cb[i] = -ref[i] * inv_su;
+          cq[i] = float4v{cb[i], cb[i], cb[i], cb[i]};
+          if (hh == 0) {
+            adj[i] = d;
+            pend = true;
+          }
           moved = true;
         }
-      } else if constexpr (st <= 6) {
+      } else if constexpr (st <= 5) {
+        // exp2 of the 8 logits over three steps (3, 3, 2)
+        constexpr int e0 = 3 * (st - 3), e1 = e0 + 3 < 8 ? e0 + 3 : 8;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k = 4 * (st - 5) + e;
-          yv[i][k] = fast_exp2(fmaf(yv[i][k], kLog2e, nbv[i]));
-          pin(yv[i][k]);
+        for (int e = e0; e < e1; ++e) {
+          const float x = sc[i][2 * hh + e / 4][e % 4];
+          yv[i][e] = fast_exp2(kScaledQ ? x : x * su);
+          pin(yv[i][e]);
         }
       } else {
+        constexpr int e0 = 4 * (st - 6);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[i][hh][e] = (_Float16)yv[i][e];
-        pin(pb[i][hh]);
+        for (int e = e0; e < e0 + 4; ++e) pb[i][hh][e] = (_Float16)yv[i][e];
+        if constexpr (st == 7) pin(pb[i][hh]);
       }
     }
   };
@@ -697,9 +719,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     const uint32_t(&kaddr)[NKO] = kaddr_s[asi];
     const uint32_t(&vaddr)[NVO] = vaddr_s[asi];
 
-    // mask values of half HH: read ahead of the stage whose LDS waits cover
-    // them (half 0 before stage A, half 1 before stage B), so each is live
-    // only until the first softmax steps of its half
+    // mask values of half HH: read ahead of the stage whose first LDS wait
+    // covers them (half 0 before stage A, half 1 before stage B); they are
+    // consumed by that stage's accumulator start
     half8 mh[TPW][2];
     auto mread = [&](auto HH) __attribute__((always_inline)) {
       constexpr int hh = decltype(HH)::value;
@@ -709,12 +731,37 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       }
     };
     mread(std::integral_constant<int, 0>{});
+    pend = false;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) adj[i] = 0.f;
 
+    // Score accumulators and their start for half HH: the mask term and minus
+    // the reference, in score units; keys past the split's end start at -inf.
+    // Called after the wait that covers the half's mask read (the empty
+    // statement keeps every read of the mask registers after that wait).
     float4v sc[TPW][4];
+    auto cinit = [&](auto HH) __attribute__((always_inline)) {
+      constexpr int hh = decltype(HH)::value;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
+      for (int i = 0; i < TPW; ++i) {
+        if constexpr (MASKMODE != kMaskNone) asm volatile("" : "+v"(mh[i][hh]));
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) sc[i][kt] = float4v{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) {
+          float4v c = cq[i];
+          if constexpr (MASKMODE != kMaskNone) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c[e] = fmaf((float)mh[i][hh][4 * j + e], mmul, cb[i]);
+          }
+          if (ragged) {   // uniform: only the block holding the split's end
+            const int k0 = kb0 + 32 * hh + 8 * g + 4 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (k0 + e >= key_end) c[e] = -INFINITY;
+          }
+          sc[i][2 * hh + j] = c;
+        }
+      }
+    };
 
     // LDS prefetch distance (steps ahead) of the K and V fragment reads:
     // deeper where the register budget allows (one tile per wave; at hd 256
@@ -723,8 +770,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     constexpr int PD = (TPW == 1 && (HD <= 128 || NW == 4)) ? 2 : 1;
 
     // S^T for half HH: K tiles kt = 2HH, 2HH+1 (keys 32HH + 8g + 4(kt%2) + 0..3
-    // in lane group g), fragments read PD steps ahead of their MFMAs.
-    // after(ks) runs after the MFMAs of step ks.
+    // in lane group g), fragments read PD steps ahead of their MFMAs; the
+    // accumulators start after the first wait.  after(ks) runs after the
+    // MFMAs of step ks.
     auto qk_half = [&](auto HH, auto after) __attribute__((always_inline)) {
       constexpr int hh = decltype(HH)::value;
       half8 kb[PD + 1][2];
@@ -741,6 +789,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
         // reads issued after those of step ks: 2 per later step in flight
         constexpr int later = (KS - 1 - ks < PD ? KS - 1 - ks : PD);
         wait_lgkm_tie<2 * later>(kb[ks % (PD + 1)][0], kb[ks % (PD + 1)][1]);
+        if constexpr (ks == 0) cinit(HH);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
@@ -791,11 +840,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     if (wave_on) {
     // A
     qk_half(H0{}, [&](auto) __attribute__((always_inline)) {});
-    // (the last wait of stage A was lgkmcnt(0): the half-0 mask has landed)
-    if (MASKMODE != kMaskNone) {
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) wait_lgkm_tie<0>(mh[i][0]);
-    }
     mread(std::integral_constant<int, 1>{});
     // B: softmax steps [8ks/KS, 8(ks+1)/KS) of half 0 after QK step ks of half 1
     qk_half(H1{}, [&](auto KSI) __attribute__((always_inline)) {
@@ -803,14 +847,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       static_for<8>([&](auto STI) __attribute__((always_inline)) {
         constexpr int stp = decltype(STI)::value;
         if constexpr (stp * KS >= 8 * ks && stp * KS < 8 * (ks + 1))
-          sm_step(STI, H0{}, ragged, mh, sc, kb0);
+          sm_step(STI, H0{}, sc);
       });
     });
-    // (the last wait of stage B was lgkmcnt(0): the half-1 mask has landed)
-    if (MASKMODE != kMaskNone) {
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) wait_lgkm_tie<0>(mh[i][1]);
-    }
     rescale();
     }
     if (first) {   // uniform: block 0's V, then the request for block 1
@@ -825,7 +864,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
       static_for<8>([&](auto STI) __attribute__((always_inline)) {
         constexpr int stp = decltype(STI)::value;
         if constexpr (stp * DT >= 8 * dt && stp * DT < 8 * (dt + 1))
-          sm_step(STI, H1{}, ragged, mh, sc, kb0);
+          sm_step(STI, H1{}, sc);
       });
     });
     rescale();
@@ -893,7 +932,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DTD; ++dt)
           __builtin_nontemporal_store(o[i][dt], (float4v *)(po + dt * 16 + 4 * g));
-        if (g == 0) a.part_ml[prow] = float2v{m_run[i] * kLog2e, l};
+        if (g == 0) a.part_ml[prow] = float2v{ref_set[i] ? ref[i] : -INFINITY, l};
       }
     }
     return;
@@ -931,7 +970,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
     const int r = tile * 16 + l16;
     if (g == 0 && r < a.M) {
       const int64_t prow = ((int64_t)inst * a.n_split + split) * a.M + r;
-      a.part_ml[prow] = float2v{m_run[i] * kLog2e, lacc[i][0]};  // max in log2 units
+      // reference in base-2 units (-inf: the row saw no key, weight 0)
+      a.part_ml[prow] = float2v{ref_set[i] ? ref[i] : -INFINITY, lacc[i][0]};
     }
   }
 }
