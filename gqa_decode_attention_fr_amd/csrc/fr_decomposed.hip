@@ -130,13 +130,18 @@ struct SoftmaxArgs {
   const float *s;
   const uint16_t *mask;
   uint16_t *p;
+  float *lsum;   // per row: the sum of the row's f16 probabilities as stored
   int64_t mask_stride;
   const int32_t *kv_len;   // per-instance valid key counts, or null
   int M, grp, n_kvh, n_tok, n_kv, kv_pad, rows;   // rows = units * M
 };
 
-// One wavefront per query row: online (max, sum) per lane over the row, then
-// a butterfly over the 64 lanes, then normalised probabilities as f16.
+// One wavefront per query row: the row max (per lane, then a butterfly over
+// the 64 lanes), then unnormalised probabilities 2^(x - max) <= 1 as f16, and
+// the row sum of exactly those f16 values.  The PV step divides by that sum,
+// so numerator and denominator see the same rounded weights: where one key
+// dominates a row, the f16 rounding of its weight cancels instead of scaling
+// the output.
 __global__ __launch_bounds__(kThreads) void softmax_kernel(SoftmaxArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -151,38 +156,27 @@ __global__ __launch_bounds__(kThreads) void softmax_kernel(SoftmaxArgs a) {
     const float mk = mrow ? (float)bits_to_half(mrow[j]) : 0.f;
     return (srow[j] + mk) * kLog2e;
   };
-  float m = -INFINITY, l = 0.f;
-  for (int j = lane; j < n_eff; j += 64) {
-    const float x = logit2(j);
-    if (x == -INFINITY) continue;
-    if (x > m) {
-      l = l * fast_exp2(m - x) + 1.f;
-      m = x;
-    } else {
-      l += fast_exp2(x - m);
-    }
-  }
+  float m = -INFINITY;
+  for (int j = lane; j < n_eff; j += 64) m = fmaxf(m, logit2(j));
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off);
-    const float l2 = __shfl_xor(l, off);
-    const float mn = fmaxf(m, m2);
-    const float a1 = (m == -INFINITY) ? 0.f : l * fast_exp2(m - mn);
-    const float a2 = (m2 == -INFINITY) ? 0.f : l2 * fast_exp2(m2 - mn);
-    l = a1 + a2;
-    m = mn;
-  }
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   uint16_t *prow = a.p + (int64_t)row * a.kv_pad;
+  float l = 0.f;
   for (int j = lane; j < a.kv_pad; j += 64) {
     float pj = 0.f;
-    if (j < n_eff && m != -INFINITY) pj = fast_exp2(logit2(j) - m) * inv;
-    prow[j] = __builtin_bit_cast(uint16_t, (_Float16)pj);
+    if (j < n_eff && m != -INFINITY) pj = fast_exp2(logit2(j) - m);
+    const _Float16 ph = (_Float16)pj;
+    l += (float)ph;
+    prow[j] = __builtin_bit_cast(uint16_t, ph);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+  if (lane == 0) a.lsum[row] = l;
 }
 
 struct PvArgs {
   const uint16_t *p;
+  const float *lsum;   // per row: the sum the probabilities are divided by
   const uint16_t *v;
   float *out;
   float *part;
@@ -269,24 +263,33 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(PvArgs a) {
   for (int i = 0; i < TILES; ++i) {
     const int r = (tile0 + i) * 16 + l16;
     if (r >= a.M) continue;
-    float *dst = (a.n_split == 1)
-                     ? a.out + (int64_t)rinst * a.out_stride +
-                           (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD
-                     : a.part + (((int64_t)inst * a.n_split + split) * a.M + r) * HD;
+    if (a.n_split == 1) {
+      // (a row with no visible key: sum 0, output 0)
+      const float l = a.lsum[(int64_t)inst * a.M + r];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float *dst = a.out + (int64_t)rinst * a.out_stride +
+                   (int64_t)instance_row(r, kvh, a.grp, a.n_head) * HD;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *(float4v *)(dst + dt * 16 + 4 * g) = o[i][dt];
+      for (int dt = 0; dt < DT; ++dt) *(float4v *)(dst + dt * 16 + 4 * g) = o[i][dt] * inv;
+    } else {
+      float *dst = a.part + (((int64_t)inst * a.n_split + split) * a.M + r) * HD;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *(float4v *)(dst + dt * 16 + 4 * g) = o[i][dt];
+    }
   }
 }
 
 struct SumArgs {
   const float *part;
+  const float *lsum;
   float *out;
   int64_t out_stride;
   int M, hd, n_split, n_inst;   // n_inst counts units
   int n_kvh, grp, n_head;
 };
 
-// out = sum over key splits of the PV partials, in split order.
+// out = sum over key splits of the PV partials, in split order, divided by
+// the row's probability sum.
 __global__ __launch_bounds__(256) void sum_kernel(SumArgs a) {
   const int q4 = a.hd / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -298,9 +301,10 @@ __global__ __launch_bounds__(256) void sum_kernel(SumArgs a) {
   for (int s = 0; s < a.n_split; ++s)
     acc += *(const float4v *)(a.part + (((int64_t)inst * a.n_split + s) * a.M + r) * a.hd +
                               4 * d4);
+  const float l = a.lsum[(int64_t)inst * a.M + r];
   const int64_t orow = (int64_t)(inst / a.n_kvh) * a.out_stride +
                        (int64_t)instance_row(r, inst % a.n_kvh, a.grp, a.n_head) * a.hd;
-  *(float4v *)(a.out + orow + 4 * d4) = acc;
+  *(float4v *)(a.out + orow + 4 * d4) = acc * (l > 0.f ? 1.f / l : 0.f);
 }
 
 template <int HD>
@@ -338,6 +342,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   if (plan.n_split > 1) part = (float *)take((size_t)U * plan.n_split * M * p.hd * 4);
   float *s = (float *)take((size_t)U * M * kv_pad * 4);
   uint16_t *pm = (uint16_t *)take((size_t)U * M * kv_pad * 2);
+  float *lsum = (float *)take((size_t)U * M * 4);
   if (off > plan.ws_bytes) return hipErrorInvalidValue;
 
   QkArgs qa;
@@ -374,6 +379,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
   sa.s = s;
   sa.mask = p.mask;
   sa.p = pm;
+  sa.lsum = lsum;
   sa.mask_stride = p.mask_stride;
   sa.M = M;
   sa.grp = p.grp();
@@ -390,6 +396,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
 
   PvArgs pa;
   pa.p = pm;
+  pa.lsum = lsum;
   pa.v = p.v;
   pa.out = p.out;
   pa.part = part;
@@ -419,6 +426,7 @@ hipError_t launch_decomposed(const Problem &p, const Plan &plan, void *workspace
 
   SumArgs ua;
   ua.part = part;
+  ua.lsum = lsum;
   ua.out = p.out;
   ua.out_stride = p.out_stride;
   ua.M = M;

@@ -92,11 +92,13 @@ int make_plan(int n_inst, int n_head, int n_tok, int n_kv, int hd, unsigned flag
     p.ws_bytes = p.n_split > 1 ? al(rows * hd * sizeof(float) + rows * 2 * sizeof(float)) : 0;
   } else {
     // [PV partials when split] [scores fp32 M x kv_pad] [probabilities f16 M x kv_pad]
+    // [probability sums fp32 M]
     const size_t kv_pad = (size_t)key_blocks * kKeyBlock;
     p.launches = 3 + (p.n_split > 1 ? 1 : 0);
     p.ws_bytes = (p.n_split > 1 ? al(rows * hd * sizeof(float)) : 0) +
                  al((size_t)n_inst * M * kv_pad * sizeof(float)) +
-                 al((size_t)n_inst * M * kv_pad * sizeof(uint16_t));
+                 al((size_t)n_inst * M * kv_pad * sizeof(uint16_t)) +
+                 al((size_t)n_inst * M * sizeof(float));
   }
   *plan = p;
   return FR_OK;
