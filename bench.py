@@ -382,7 +382,9 @@ def machine_probes(torch):
     lib.frp_merge.argtypes = [i32, vp, vp, vp, vp, i32, i32, vp]
     lib.frp_lds.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.frp_read_shared.argtypes = [vp, i64, i32, i32, vp, vp, vp]
-    for f in (lib.frp_empty, lib.frp_read, lib.frp_merge, lib.frp_lds, lib.frp_read_shared):
+    lib.frp_issue.argtypes = [i32, i32, i32, vp, vp, vp]
+    for f in (lib.frp_empty, lib.frp_read, lib.frp_merge, lib.frp_lds, lib.frp_read_shared,
+              lib.frp_issue):
         f.restype = i32
     grid, pf, wb = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     lib.frp_merge_sizes(ctypes.byref(grid), ctypes.byref(pf), ctypes.byref(wb))
@@ -473,7 +475,20 @@ def machine_probes(torch):
             tt = t2.cpu().numpy()
             res[f"lds_{kname}_bytes_per_ns_{lanes // 256}_waves_per_simd"] = round(
                 iters * 16 * per_lane * lanes / ((tt[1] - tt[0]) * 10.0), 1)
-    del t2, s2
+    # how matrix-core and vector-ALU work share a SIMD: ns per trip of 8 MFMAs
+    # (16x16x32 f16) and/or 32 fp32 fma, alone, interleaved in one wave, or in
+    # two waves of one SIMD (one MFMA wave, one VALU wave)
+    sf = torch.zeros(1, dtype=torch.float32, device="cuda")
+    for mode, lanes, label in ((0, 256, "mfma8_1_wave_per_simd"), (1, 256, "fma32_1_wave_per_simd"),
+                               (2, 256, "mfma8_and_fma32_same_wave"),
+                               (0, 512, "mfma8_2_waves_per_simd"), (1, 512, "fma32_2_waves_per_simd"),
+                               (3, 512, "mfma8_wave_and_fma32_wave_per_simd")):
+        iters = 20000
+        ok(lib.frp_issue(mode, lanes, iters, t2.data_ptr(), sf.data_ptr(), stream), "issue")
+        torch.cuda.synchronize()
+        tt = t2.cpu().numpy()
+        res[f"issue_ns_per_trip_{label}"] = round(float(tt[1] - tt[0]) * 10.0 / iters, 2)
+    del t2, s2, sf
 
     # merging key-split partials: two launches against one
     part = torch.zeros(grid * pf, dtype=torch.float32, device="cuda")

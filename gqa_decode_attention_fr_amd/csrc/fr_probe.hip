@@ -1,8 +1,9 @@
 // fr_probe.hip -- measurement probes for the benchmark, built as libfrprobe.so
 // apart from the attention library: the launch floor of an empty kernel, the
-// HBM read rate one compute unit and the whole chip reach, and the cost of
-// merging key-split partials inside one kernel against a second launch.  None
-// of it is on the attention path; bench.py reports what it measures.
+// HBM read rate one compute unit and the whole chip reach, LDS read rates, how
+// matrix-core and vector-ALU work share a SIMD, and the cost of merging
+// key-split partials inside one kernel against a second launch.  None of it is
+// on the attention path; bench.py reports what it measures.
 //
 // Every launch has a fixed, host-checked grid.  The split workgroups never
 // wait; the one-launch merges count arrivals and let the last arriver merge,
@@ -126,6 +127,59 @@ __global__ __launch_bounds__(NT) void lds_read_kernel(uint64_t *times, uint32_t 
     times[1] = t1;
   }
   if (acc == 0xdeadbeefu) sink[0] = acc;
+}
+
+// ---- issue probe: how matrix-core (MFMA) and vector-ALU work share a SIMD.
+// One workgroup of NT lanes (one or two waves per SIMD); each trip of a wave:
+//   MODE 0: 8 v_mfma_f32_16x16x32_f16 (four accumulation chains)
+//   MODE 1: 32 independent fp32 fma
+//   MODE 2: both, interleaved in the same wave
+//   MODE 3: (two waves per SIMD) waves 0-3 the 32 fma, waves 4-7 the 8 MFMAs
+// times[0], times[1] bracket `iters` trips (100 MHz counter).
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+template <int MODE, int NT>
+__global__ __launch_bounds__(NT) void issue_kernel(uint64_t *times, float *sink, int iters) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const half8 a = {(_Float16)(lane * 1e-3f), 0, 0, 0, 0, 0, 0, (_Float16)1};
+  const half8 b = {(_Float16)1, 0, 0, 0, 0, 0, 0, (_Float16)(lane * 1e-3f)};
+  float4v c[4] = {};
+  float x[32];
+  for (int i = 0; i < 32; ++i) x[i] = lane * 1e-3f + i;
+  const bool do_m = MODE == 0 || MODE == 2 || (MODE == 3 && wave >= 4);
+  const bool do_v = MODE == 1 || MODE == 2 || (MODE == 3 && wave < 4);
+  __syncthreads();
+  const uint64_t t0 = clock100();
+  if (do_m && do_v) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        c[k & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[k & 3], 0, 0, 0);
+#pragma unroll
+        for (int i = 4 * k; i < 4 * k + 4; ++i) x[i] = __builtin_fmaf(x[i], 0.999f, 0.5f);
+      }
+    }
+  } else if (do_m) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        c[k & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[k & 3], 0, 0, 0);
+    }
+  } else if (do_v) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], 0.999f, 0.5f);
+    }
+  }
+  __syncthreads();
+  const uint64_t t1 = clock100();
+  if (threadIdx.x == 0) {
+    times[0] = t0;
+    times[1] = t1;
+  }
+  float acc = c[0][0] + c[1][1] + c[2][2] + c[3][3];
+  for (int i = 0; i < 32; ++i) acc += x[i];
+  if (acc == 1234.5f) sink[0] = acc;
 }
 
 // ---- merge probe.  kMergeGrid workgroups of 256 lanes form groups of n_split
@@ -400,6 +454,29 @@ int frp_lds(int kind, int lanes, int iters, uint64_t *times, uint32_t *sink, voi
     hipLaunchKernelGGL((lds_read_kernel<1, 256>), dim3(1), dim3(256), 0, s, times, sink, iters);
   else
     hipLaunchKernelGGL((lds_read_kernel<1, 512>), dim3(1), dim3(512), 0, s, times, sink, iters);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// One workgroup of the issue probe: mode 0..2 with 256 or 512 lanes, mode 3
+// with 512; times 2 uint64, sink 1 float.
+int frp_issue(int mode, int lanes, int iters, uint64_t *times, float *sink, void *stream) {
+  if (!times || !sink || iters < 1 || mode < 0 || mode > 3 || (lanes != 256 && lanes != 512) ||
+      (mode == 3 && lanes != 512))
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(1), dim3(lanes), 0, s, times, sink, iters);
+  };
+  if (lanes == 256) {
+    if (mode == 0) go(issue_kernel<0, 256>);
+    if (mode == 1) go(issue_kernel<1, 256>);
+    if (mode == 2) go(issue_kernel<2, 256>);
+  } else {
+    if (mode == 0) go(issue_kernel<0, 512>);
+    if (mode == 1) go(issue_kernel<1, 512>);
+    if (mode == 2) go(issue_kernel<2, 512>);
+    if (mode == 3) go(issue_kernel<3, 512>);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
