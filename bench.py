@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -50,11 +51,20 @@ KERNEL_SOURCES = ["gqa_decode_attention_fr_amd/csrc/fr_fused.hip",
                   "gqa_decode_attention_fr_amd/csrc/fr_qkv.hip"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks or empty lines: what the
+    compiler sees (a comment edit leaves the kernels, and their counters, as
+    they were)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines())
+    return "\n".join(l for l in lines if l)
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

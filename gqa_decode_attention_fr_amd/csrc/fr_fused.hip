@@ -537,7 +537,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void split_kernel(SplitArgs a) {
 
   // Online-softmax state of each tile row, in "score units" u: the scores the
   // matrix core produces are base-2 logits times 1/su, where su = 1 for split
-  // queries (they carry scale*log2(e)) and su = scale*log2(e) for f16 queries.
+  // queries (they carry scale*log2(e)) and su = scale*log2(e) for f16 queries
+  // (given as f16, or f32 rounded once).
   //   ref: the reference max (base-2 logit units), 0 until the row has seen a
   //        key (ref_set false), then moved up only by more than kLazy2
   //   cb:  -ref/su, the reference as it enters the score accumulator; cq is
