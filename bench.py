@@ -806,9 +806,9 @@ def run_qkv_workload(args, torch, F):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-              "supported (independent instances or KV shards would each run this kernel on "
-              "their own GPU).", file=sys.stderr)
+        print(f"bench.py: the library and this benchmark run on one GPU; --gpus {args.gpus} "
+              "is not supported (independent instances or KV shards would each run this "
+              "kernel on their own GPU).", file=sys.stderr)
         return 2
     import torch
 
